@@ -1,0 +1,158 @@
+// Communication units: the local data movement of one GPU's share of the
+// collectives, done by ordinary workgroups with 16-byte vector loads and
+// stores (bandwidth-bound, no LDS).
+//
+//   all_gather (Iris docs "Fused Communication and Compute Operations",
+//   all_gather_matmul): shard s of rank order lands in columns
+//   [s*K_local, (s+1)*K_local) of the gathered matrix. Unit (pm, s) copies
+//   rows [pm*BM, pm*BM+BM) of shard s. Bit copy.
+//
+//   reduce (same page, matmul_reduce_scatter and matmul_all_reduce; the
+//   all_reduce beside an independent GEMM of the iris.concurrent PR):
+//   out = own + sum of the other ranks' partial buffers, in that order,
+//   accumulated in fp32 and rounded once to fp16. A unit is a rectangle of
+//   rows x columns (reduce_scatter / matmul_all_reduce) or a flat chunk
+//   (concurrent all_reduce).
+//
+// Each thread moves 8 fp16 (16 bytes) per vector and keeps several vectors
+// in flight; a wavefront covers 1 KiB of contiguous row per load, and every
+// wavefront reduces its own vectors with no cross-lane traffic.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace iris {
+
+struct CommArgs {
+  const f16* src[kMaxW];  // shards (AG) / partials (RS, AR) / buffers (concurrent)
+  int32_t W;              // number of src buffers used
+  f16* dst;               // gathered (AG) / out
+  // all_gather
+  int64_t K_local, K;     // shard row length, gathered row length
+  // 2-D reduce: out[m][j] = C[m][col0 + j] + sum_p src[p][m][j]
+  const f16* C;
+  int64_t ldc;
+  int32_t col0;           // rank * N_local (RS) or 0 (AR)
+  int32_t ncols;          // N_local (RS) or N (AR): row length of src and dst
+  int32_t comm_bn;        // columns per unit
+  int32_t n_cc;           // column chunks per row block
+  // flat all_reduce
+  int64_t elems;
+  int32_t chunk;
+  int32_t M, BM;
+};
+
+// ------------------------------------------------------------- all_gather
+template <int U>
+__device__ void ag_copy_unit(const CommArgs& a, int pm, int s) {
+  const int r0 = pm * a.BM;
+  const int rows = min(a.BM, a.M - r0);
+  if (rows <= 0) return;
+  const uint32_t vpr = (uint32_t)(a.K_local >> 3);  // 16-byte vectors per row
+  const uint32_t total = (uint32_t)rows * vpr;
+  const FastDiv fd = FastDiv::make(vpr);
+  const f16* src = a.src[s] + (int64_t)r0 * a.K_local;  // rows are contiguous
+  f16* dst = a.dst + (int64_t)r0 * a.K + (int64_t)s * a.K_local;
+  for (uint32_t base = threadIdx.x; base < total; base += kThreads * U) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t i = base + u * kThreads;
+      if (i < total) v[u] = ld16(src + (int64_t)i * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t i = base + u * kThreads;
+      if (i < total) {
+        const uint32_t r = fd.div(i);
+        const uint32_t c = i - r * vpr;
+        st16(dst + (int64_t)r * a.K + c * 8, v[u]);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void add8(float acc[8], u32x4 v) {
+  const f16x8 h = as_h8(v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] += (float)h[e];
+}
+
+__device__ __forceinline__ u32x4 round8(const float acc[8]) {
+  f16x8 h;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = (f16)acc[e];
+  return as_u4(h);
+}
+
+// --------------------------------------------------------------- 2-D reduce
+// Unit (pm, cc): rows [pm*BM, +BM), columns [cc*comm_bn, +comm_bn) of the
+// (M x ncols) output; own values come from C at column offset col0.
+template <int U>
+__device__ void reduce2d_unit(const CommArgs& a, int pm, int cc) {
+  const int r0 = pm * a.BM;
+  const int rows = min(a.BM, a.M - r0);
+  const int j0 = cc * a.comm_bn;
+  const int cols = min(a.comm_bn, a.ncols - j0);
+  if (rows <= 0 || cols <= 0) return;
+  const uint32_t vpr = (uint32_t)(cols >> 3);
+  const uint32_t total = (uint32_t)rows * vpr;
+  const FastDiv fd = FastDiv::make(vpr);
+  for (uint32_t base = threadIdx.x; base < total; base += kThreads * U) {
+    float acc[U][8];
+    int64_t orow[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t i = base + u * kThreads;
+      ok[u] = i < total;
+      const uint32_t r = fd.div(i);
+      const uint32_t c = i - r * vpr;
+      orow[u] = (int64_t)(r0 + r) * a.ncols + j0 + c * 8;  // index into src/dst
+      const int64_t cidx = (int64_t)(r0 + r) * a.ldc + a.col0 + j0 + c * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[u][e] = 0.0f;
+      if (ok[u]) add8(acc[u], ld16(a.C + cidx));
+    }
+    for (int p = 0; p < a.W; ++p) {
+      const f16* sp = a.src[p];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (ok[u]) add8(acc[u], ld16(sp + orow[u]));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (ok[u]) st16(a.dst + orow[u], round8(acc[u]));
+  }
+}
+
+// ----------------------------------------------------------- flat reduce
+// Unit u: elements [u*chunk, min((u+1)*chunk, elems)); dst = sum_w src[w].
+template <int U>
+__device__ void reduce_flat_unit(const CommArgs& a, int u) {
+  const int64_t e0 = (int64_t)u * a.chunk;
+  const int64_t n = min((int64_t)a.chunk, a.elems - e0);
+  if (n <= 0) return;
+  const uint32_t total = (uint32_t)(n >> 3);
+  for (uint32_t base = threadIdx.x; base < total; base += kThreads * U) {
+    float acc[U][8];
+    bool ok[U];
+#pragma unroll
+    for (int v = 0; v < U; ++v) {
+      ok[v] = base + v * kThreads < total;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[v][e] = 0.0f;
+    }
+    for (int w = 0; w < a.W; ++w) {
+      const f16* sp = a.src[w] + e0;
+#pragma unroll
+      for (int v = 0; v < U; ++v)
+        if (ok[v]) add8(acc[v], ld16(sp + (int64_t)(base + v * kThreads) * 8));
+    }
+#pragma unroll
+    for (int v = 0; v < U; ++v)
+      if (ok[v]) st16(a.dst + e0 + (int64_t)(base + v * kThreads) * 8, round8(acc[v]));
+  }
+}
+
+}  // namespace iris

@@ -1,0 +1,790 @@
+// C-ABI host library: validation, configuration, workspace, launch and the
+// gemm_wgs sweep for one GPU's share of the fused communication + GEMM ops.
+//
+// Operation definitions: Iris docs "Fused Communication and Compute
+// Operations" (all_gather_matmul, matmul_reduce_scatter, matmul_all_reduce).
+// Scheduling knobs, fused/sequential modes and the tuning policy (benchmark
+// the candidates including the static default, keep the winner in a cache
+// written to a temporary file then renamed, ignore a failed write, key by
+// the device's gcnArchName): ROCm/iris PR "Add iris.concurrent (concurrent,
+// independent, fused comm+gemm)", description and its autotune code excerpts.
+// config == NULL selecting a configuration automatically and the NN-only
+// layout: ROCm/iris PR "Add auto-config selection for fused AG+matmul with
+// 28 tuned HBM buffer configs", summary.
+#include "../../include/iris_local.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cerrno>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <sys/stat.h>
+#include <unistd.h>
+#include <vector>
+
+#include "launch.hpp"
+
+namespace {
+
+using iris::Params;
+
+thread_local std::string g_msg;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_msg = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(IRIS_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+// ------------------------------------------------------------ device facts
+struct DevInfo {
+  bool ok = false;
+  int cus = 0;
+  int clock_khz = 0, mem_clock_khz = 0, wall_khz = 0, lds = 0;
+  int64_t mem = 0;
+  std::string arch;
+};
+
+std::mutex g_mu;
+std::map<int, DevInfo> g_dev;
+
+int current_device(int* dev, DevInfo* info) {
+  int d = 0;
+  hipError_t e = hipGetDevice(&d);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_dev.find(d);
+    if (it != g_dev.end()) {
+      *dev = d;
+      *info = it->second;
+      return IRIS_OK;
+    }
+  }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, d);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  DevInfo di;
+  di.cus = prop.multiProcessorCount;
+  di.clock_khz = prop.clockRate;
+  di.mem_clock_khz = prop.memoryClockRate;
+  di.lds = (int)prop.maxSharedMemoryPerMultiProcessor;
+  di.mem = (int64_t)prop.totalGlobalMem;
+  di.arch = prop.gcnArchName;
+  int wall = 0;
+  if (hipDeviceGetAttribute(&wall, hipDeviceAttributeWallClockRate, d) != hipSuccess) wall = 100000;
+  di.wall_khz = wall > 0 ? wall : 100000;
+  di.ok = di.arch.rfind("gfx950", 0) == 0;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_dev[d] = di;
+  }
+  *dev = d;
+  *info = di;
+  if (!di.ok) return fail(IRIS_ERR_NO_DEVICE, "device %d is %s; this library is built for gfx950", d, di.arch.c_str());
+  return IRIS_OK;
+}
+
+// ------------------------------------------------------------ tuning cache
+std::string cache_path() {
+  const char* p = getenv("IRIS_LOCAL_TUNE_CACHE");
+  if (p && *p) return p;
+  const char* home = getenv("HOME");
+  return std::string(home && *home ? home : "/tmp") + "/.cache/iris_local/tune.txt";
+}
+
+std::string cache_key(const std::string& arch, int op, int64_t M, int64_t N, int64_t K, int W, int bm,
+                      int bn, int bk, int gm) {
+  char buf[256];
+  std::string a = arch.substr(0, arch.find(':'));
+  snprintf(buf, sizeof buf, "%s op%d M%lld N%lld K%lld W%d t%dx%dx%d g%d", a.c_str(), op, (long long)M,
+           (long long)N, (long long)K, W, bm, bn, bk, gm);
+  return buf;
+}
+
+std::map<std::string, int> load_cache() {
+  std::map<std::string, int> db;
+  FILE* f = fopen(cache_path().c_str(), "r");
+  if (!f) return db;
+  char line[512];
+  while (fgets(line, sizeof line, f)) {
+    char* eq = strrchr(line, '=');
+    if (!eq) continue;
+    *eq = 0;
+    std::string key(line);
+    while (!key.empty() && key.back() == ' ') key.pop_back();
+    db[key] = atoi(eq + 1);
+  }
+  fclose(f);
+  return db;
+}
+
+void mkdirs(const std::string& path) {
+  for (size_t i = 1; i < path.size(); ++i)
+    if (path[i] == '/') mkdir(path.substr(0, i).c_str(), 0755);
+}
+
+void save_cache_entry(const std::string& key, int value) {
+  std::map<std::string, int> db = load_cache();
+  db[key] = value;
+  const std::string path = cache_path();
+  mkdirs(path);
+  const std::string tmp = path + "." + std::to_string(getpid()) + ".tmp";
+  FILE* f = fopen(tmp.c_str(), "w");
+  if (!f) return;  // an unwritable cache only loses the memo
+  bool ok = true;
+  for (auto& kv : db) ok = ok && fprintf(f, "%s = %d\n", kv.first.c_str(), kv.second) > 0;
+  ok = (fclose(f) == 0) && ok;
+  if (!ok || rename(tmp.c_str(), path.c_str()) != 0) unlink(tmp.c_str());
+}
+
+// --------------------------------------------------------------- config
+struct Resolved {
+  int bm, bn, bk, gm, gemm_wgs, comm_bn, comm_chunk, mode, flags;
+  int grid;
+};
+
+constexpr int kDefaultTile = 256;
+constexpr int kDefaultGroupM = 8;
+constexpr int kDefaultChunk = 65536;
+
+int iris_op_to_kind(int op) {
+  switch (op) {
+    case IRIS_OP_AG_MM: return iris::OP_AG;
+    case IRIS_OP_MM_RS: return iris::OP_RS;
+    case IRIS_OP_MM_AR: return iris::OP_ARMM;
+    case IRIS_OP_CONCURRENT: return iris::OP_CONC_AR;
+  }
+  return -1;
+}
+
+// Validates and fills everything but the grid / gemm_wgs (device-dependent).
+int resolve_static(const iris_config_t* cfg, Resolved* r) {
+  iris_config_t c{};
+  if (cfg) c = *cfg;
+  r->bm = c.block_m > 0 ? c.block_m : kDefaultTile;
+  r->bn = c.block_n > 0 ? c.block_n : kDefaultTile;
+  if (c.block_m <= 0 && c.block_n > 0) r->bm = c.block_n == 64 ? 64 : (c.block_n == 128 ? 128 : 256);
+  if (c.block_n <= 0 && c.block_m > 0) r->bn = c.block_m == 64 ? 64 : (c.block_m == 128 ? 128 : 256);
+  r->bk = c.block_k > 0 ? c.block_k : 64;
+  r->gm = c.group_m > 0 ? c.group_m : kDefaultGroupM;
+  r->gemm_wgs = c.gemm_wgs;
+  r->comm_bn = c.comm_block_n > 0 ? c.comm_block_n : r->bn;
+  r->comm_chunk = c.comm_chunk > 0 ? c.comm_chunk : kDefaultChunk;
+  r->mode = c.mode;
+  r->flags = c.flags;
+  if (!iris::tile_supported(r->bm, r->bn))
+    return fail(IRIS_ERR_CONFIG, "unsupported GEMM tile %dx%d (supported: 256x256, 256x128, 128x128, 64x64)",
+                r->bm, r->bn);
+  if (r->bk != 64) return fail(IRIS_ERR_CONFIG, "block_k must be 64 (got %d)", r->bk);
+  if (r->gm > 1 << 16) return fail(IRIS_ERR_CONFIG, "group_m too large (%d)", r->gm);
+  if (r->comm_bn % 8 != 0) return fail(IRIS_ERR_CONFIG, "comm_block_n must be a multiple of 8 (got %d)", r->comm_bn);
+  if (r->comm_chunk % 2048 != 0) return fail(IRIS_ERR_CONFIG, "comm_chunk must be a multiple of 2048 (got %d)", r->comm_chunk);
+  if (r->mode != IRIS_MODE_FUSED && r->mode != IRIS_MODE_SEQUENTIAL)
+    return fail(IRIS_ERR_CONFIG, "unknown mode %d", r->mode);
+  if (r->flags & ~(IRIS_FLAG_NO_STEAL | IRIS_FLAG_BIAS_ALONG_M))
+    return fail(IRIS_ERR_CONFIG, "unknown flag bits 0x%x", r->flags);
+  return IRIS_OK;
+}
+
+int resolve_device(Resolved* r, int kind, const DevInfo& di, const std::string& key) {
+  const int occ = iris::persistent_blocks_per_cu(r->bm, r->bn, kind);
+  if (occ <= 0) return fail(IRIS_ERR_HIP, "occupancy query failed for tile %dx%d", r->bm, r->bn);
+  r->grid = di.cus * occ;
+  if (r->grid > 2048) r->grid = 2048;
+  if (r->gemm_wgs <= 0) {
+    int tuned = 0;
+    if (r->mode == IRIS_MODE_FUSED) {
+      std::map<std::string, int> db = load_cache();
+      auto it = db.find(key);
+      if (it != db.end()) tuned = it->second;
+    }
+    r->gemm_wgs = (tuned > 0 && tuned < r->grid) ? tuned : (r->grid * 7) / 8;
+  }
+  if (r->mode == IRIS_MODE_FUSED && (r->gemm_wgs < 1 || r->gemm_wgs > r->grid - 1))
+    return fail(IRIS_ERR_CONFIG, "gemm_wgs %d outside [1, %d] for a grid of %d workgroups", r->gemm_wgs,
+                r->grid - 1, r->grid);
+  return IRIS_OK;
+}
+
+// ------------------------------------------------------------- workspace
+constexpr int kMaxGrid = 2048;
+constexpr size_t kStampBytes = (size_t)kMaxGrid * 4 * sizeof(uint64_t);
+
+int64_t flag_words(int kind, int64_t M, int64_t N, int W, int bm, int bn) {
+  const int64_t n_pm = (M + bm - 1) / bm, n_pn = (N + bn - 1) / bn;
+  if (kind == iris::OP_AG) return n_pm * W;
+  if (kind == iris::OP_RS || kind == iris::OP_ARMM) return n_pm * n_pn;
+  return 0;
+}
+
+size_t int_region_bytes(int64_t words) {
+  const size_t b = (size_t)(iris::kFlagBase + words) * 4;
+  return (b + 255) & ~(size_t)255;
+}
+
+struct OwnedWs {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::map<std::pair<int, void*>, OwnedWs> g_ws;   // (device, stream) -> workspace
+struct LastLaunch {
+  int dev;
+  int grid;          // workgroups of the persistent launch
+  bool fused;
+  size_t stamp_off;  // byte offset of the stamps in the workspace
+};
+std::map<void*, LastLaunch> g_last;  // workspace -> its last launch
+
+int get_workspace(int dev, void* stream, size_t need, void* user, size_t user_bytes, void** out) {
+  if (user) {
+    if (user_bytes < need)
+      return fail(IRIS_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", user_bytes, need);
+    if ((uintptr_t)user % 256 != 0) return fail(IRIS_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+    *out = user;
+    return IRIS_OK;
+  }
+  std::lock_guard<std::mutex> lk(g_mu);
+  OwnedWs& w = g_ws[{dev, stream}];
+  if (w.bytes < need) {
+    if (w.ptr) {
+      // the old buffer may still be in use by enqueued work on this stream
+      hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+      if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+      (void)hipFree(w.ptr);
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    size_t bytes = std::max(need, (size_t)1 << 20);
+    hipError_t e = hipMalloc(&w.ptr, bytes);
+    if (e != hipSuccess) {
+      w.ptr = nullptr;
+      return fail(IRIS_ERR_NO_MEMORY, "hipMalloc of a %zu-byte workspace failed: %s", bytes, hipGetErrorString(e));
+    }
+    w.bytes = bytes;
+  }
+  *out = w.ptr;
+  return IRIS_OK;
+}
+
+// ------------------------------------------------------------ validation
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+int check_ptr(const void* p, const char* name, bool required = true) {
+  if (!p) return required ? fail(IRIS_ERR_INVALID_ARG, "%s is NULL", name) : IRIS_OK;
+  if (!aligned16(p)) return fail(IRIS_ERR_ALIGNMENT, "%s is not 16-byte aligned", name);
+  return IRIS_OK;
+}
+
+int check_gemm_dims(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return fail(IRIS_ERR_INVALID_ARG, "M, N, K must be positive (got %lld, %lld, %lld)",
+                                               (long long)M, (long long)N, (long long)K);
+  if (M > (1 << 30) || N > (1 << 21) || K > (1 << 21))
+    return fail(IRIS_ERR_UNSUPPORTED, "shape too large (limits: M <= 2^30, N <= 2^21, K <= 2^21)");
+  if (N % 8 != 0 || K % 8 != 0)
+    return fail(IRIS_ERR_ALIGNMENT, "N and K must be multiples of 8 (got N=%lld, K=%lld)", (long long)N, (long long)K);
+  return IRIS_OK;
+}
+
+// ---------------------------------------------------------------- launch
+struct OpDesc {
+  int kind;  // iris::OpKind
+  void* C;
+  void* out;
+  const void* A;
+  const void* const* srcs;
+  int W;      // ranks (AG: shards; RS/AR: ranks incl. own; concurrent: buffers)
+  int rank;
+  const void* B;
+  const void* bias;
+  int64_t M, N, K;  // K = full contraction length
+  int64_t K_local;
+  int64_t comm_elems;
+};
+
+int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_bytes, void* stream,
+        Resolved* used = nullptr) {
+  Resolved r{};
+  int st = resolve_static(cfg, &r);
+  if (st) return st;
+  int dev = 0;
+  DevInfo di;
+  st = current_device(&dev, &di);
+  if (st) return st;
+  const int iris_op = d.kind == iris::OP_AG ? IRIS_OP_AG_MM
+                      : d.kind == iris::OP_RS ? IRIS_OP_MM_RS
+                      : d.kind == iris::OP_ARMM ? IRIS_OP_MM_AR
+                                                : IRIS_OP_CONCURRENT;
+  const std::string key =
+      cache_key(di.arch, iris_op, d.M, d.N, d.kind == iris::OP_AG ? d.K_local : d.K, d.W, r.bm, r.bn, r.bk, r.gm);
+  st = resolve_device(&r, d.kind, di, key);
+  if (st) return st;
+  if (used) *used = r;
+
+  const int64_t words = flag_words(d.kind, d.M, d.N, d.W, r.bm, r.bn);
+  const size_t ibytes = int_region_bytes(words);
+  void* ws = nullptr;
+  st = get_workspace(dev, stream, ibytes + kStampBytes, workspace, ws_bytes, &ws);
+  if (st) return st;
+
+  Params p;
+  memset(&p, 0, sizeof p);
+  iris::GemmArgs& g = p.g;
+  g.A = (const iris::f16*)(d.kind == iris::OP_AG ? d.out : d.A);
+  g.lda = d.K;
+  g.B = (const iris::f16*)d.B;
+  g.ldb = d.N;
+  g.bias = (const iris::f16*)d.bias;
+  g.bias_along_m = (r.flags & IRIS_FLAG_BIAS_ALONG_M) ? 1 : 0;
+  g.C = (iris::f16*)d.C;
+  g.ldc = d.N;
+  g.M = (int)d.M;
+  g.N = (int)d.N;
+  g.K = (int)d.K;
+  p.n_pm = (int)((d.M + r.bm - 1) / r.bm);
+  p.n_pn = (int)((d.N + r.bn - 1) / r.bn);
+  p.group_m = r.gm;
+  p.T_gemm = p.n_pm * p.n_pn;
+  iris::CommArgs& c = p.c;
+  c.M = (int)d.M;
+  c.BM = r.bm;
+  switch (d.kind) {
+    case iris::OP_AG:
+      c.W = d.W;
+      for (int s = 0; s < d.W; ++s) c.src[s] = (const iris::f16*)d.srcs[s];
+      c.dst = (iris::f16*)d.out;
+      c.K_local = d.K_local;
+      c.K = d.K;
+      p.T_comm = p.n_pm * d.W;
+      break;
+    case iris::OP_RS:
+    case iris::OP_ARMM: {
+      const int64_t nl = d.kind == iris::OP_RS ? d.N / d.W : d.N;
+      c.W = d.W - 1;
+      for (int s = 0; s < d.W - 1; ++s) c.src[s] = (const iris::f16*)d.srcs[s];
+      c.dst = (iris::f16*)d.out;
+      c.C = (const iris::f16*)d.C;
+      c.ldc = d.N;
+      c.col0 = d.kind == iris::OP_RS ? (int)(d.rank * nl) : 0;
+      c.ncols = (int)nl;
+      c.comm_bn = r.comm_bn;
+      c.n_cc = (int)((nl + r.comm_bn - 1) / r.comm_bn);
+      p.T_comm = p.n_pm * c.n_cc;
+      // GEMM tiles feeding this rank's slice go first
+      p.prio_lo = c.col0 / r.bn;
+      p.prio_hi = (int)((c.col0 + nl + r.bn - 1) / r.bn);
+      break;
+    }
+    case iris::OP_CONC_AR:
+      c.W = d.W;
+      for (int s = 0; s < d.W; ++s) c.src[s] = (const iris::f16*)d.srcs[s];
+      c.dst = (iris::f16*)d.out;
+      c.elems = d.comm_elems;
+      c.chunk = r.comm_chunk;
+      p.T_comm = (int)((d.comm_elems + r.comm_chunk - 1) / r.comm_chunk);
+      break;
+  }
+  p.ws = (int32_t*)ws;
+  p.stamps = (uint64_t*)((char*)ws + ibytes);
+  p.spin_limit = 1u << 24;
+  p.steal = (r.flags & IRIS_FLAG_NO_STEAL) ? 0 : 1;
+  const hipStream_t s = (hipStream_t)stream;
+
+  hipError_t e = iris::launch_reset(p.ws, (int)(ibytes / 4), s);
+  if (e != hipSuccess) return hip_fail(e, "reset launch");
+  if (r.mode == IRIS_MODE_FUSED) {
+    p.op = d.kind;
+    p.fused = 1;
+    p.gemm_wgs = r.gemm_wgs;
+    e = iris::launch_persistent(p, r.bm, r.bn, r.grid, s);
+    if (e != hipSuccess) return hip_fail(e, "fused launch");
+  } else {
+    // unfused baseline: the comm kernel and the GEMM kernel each get the
+    // whole GPU, in dependency order (gather before GEMM; GEMM before reduce)
+    Params pg = p;
+    pg.op = iris::OP_GEMM;
+    pg.fused = 0;
+    pg.T_comm = 0;
+    pg.gemm_wgs = r.grid;
+    Params pc = p;
+    pc.op = d.kind;
+    pc.fused = 0;
+    const int comm_grid = di.cus * 4;
+    if (d.kind == iris::OP_AG) {
+      e = iris::launch_comm_only(pc, comm_grid, s);
+      if (e == hipSuccess) e = iris::launch_persistent(pg, r.bm, r.bn, r.grid, s);
+    } else {
+      e = iris::launch_persistent(pg, r.bm, r.bn, r.grid, s);
+      if (e == hipSuccess) e = iris::launch_comm_only(pc, comm_grid, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "sequential launch");
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_last[ws] = LastLaunch{dev, r.grid, r.mode == IRIS_MODE_FUSED, ibytes};
+  }
+  if (getenv("IRIS_LOCAL_DEBUG")) {
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "debug sync");
+    int32_t err = 0;
+    e = hipMemcpy(&err, p.ws + iris::kErr, 4, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "debug readback");
+    if (err) return fail(IRIS_ERR_DEVICE_TIMEOUT, "a device-side wait hit its poll bound");
+  }
+  return IRIS_OK;
+}
+
+int copy_ptrs(const void* const* arr, int n, const char* name) {
+  if (n > 0 && !arr) return fail(IRIS_ERR_INVALID_ARG, "%s array is NULL", name);
+  for (int i = 0; i < n; ++i) {
+    char nm[64];
+    snprintf(nm, sizeof nm, "%s[%d]", name, i);
+    int st = check_ptr(arr[i], nm);
+    if (st) return st;
+  }
+  return IRIS_OK;
+}
+
+}  // namespace
+
+// ====================================================================== ABI
+extern "C" {
+
+int iris_ag_mm(void* C, void* A_gathered, const void* const* A_shards, int32_t W, const void* B,
+               const void* bias, int64_t M, int64_t N, int64_t K_local, const iris_config_t* cfg,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  g_msg.clear();
+  if (W < 1 || W > IRIS_MAX_W) return fail(IRIS_ERR_INVALID_ARG, "W must be in [1, %d] (got %d)", IRIS_MAX_W, W);
+  int st;
+  if ((st = check_ptr(C, "C")) || (st = check_ptr(A_gathered, "A_gathered")) || (st = check_ptr(B, "B")) ||
+      (st = check_ptr(bias, "bias", false)) || (st = copy_ptrs(A_shards, W, "A_shards")))
+    return st;
+  if (K_local <= 0) return fail(IRIS_ERR_INVALID_ARG, "K_local must be positive");
+  if (K_local % 8 != 0) return fail(IRIS_ERR_ALIGNMENT, "K_local must be a multiple of 8 (got %lld)", (long long)K_local);
+  if ((st = check_gemm_dims(M, N, K_local * W))) return st;
+  OpDesc d{};
+  d.kind = iris::OP_AG;
+  d.C = C;
+  d.out = A_gathered;
+  d.srcs = A_shards;
+  d.W = W;
+  d.B = B;
+  d.bias = bias;
+  d.M = M;
+  d.N = N;
+  d.K = K_local * W;
+  d.K_local = K_local;
+  return run(d, cfg, workspace, workspace_bytes, stream);
+}
+
+int iris_mm_rs_local(void* out, void* C, const void* A, const void* B, const void* bias,
+                     const void* const* partials, int32_t W, int32_t rank, int64_t M, int64_t N, int64_t K,
+                     const iris_config_t* cfg, void* workspace, size_t workspace_bytes, void* stream) {
+  g_msg.clear();
+  if (W < 1 || W > IRIS_MAX_W) return fail(IRIS_ERR_INVALID_ARG, "W must be in [1, %d] (got %d)", IRIS_MAX_W, W);
+  if (rank < 0 || rank >= W) return fail(IRIS_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, W);
+  int st;
+  if ((st = check_ptr(out, "out")) || (st = check_ptr(C, "C")) || (st = check_ptr(A, "A")) ||
+      (st = check_ptr(B, "B")) || (st = check_ptr(bias, "bias", false)) || (st = copy_ptrs(partials, W - 1, "partials")))
+    return st;
+  if ((st = check_gemm_dims(M, N, K))) return st;
+  if (N % W != 0) return fail(IRIS_ERR_INVALID_ARG, "N (%lld) must be divisible by W (%d)", (long long)N, W);
+  if ((N / W) % 8 != 0) return fail(IRIS_ERR_ALIGNMENT, "N/W must be a multiple of 8 (got %lld)", (long long)(N / W));
+  OpDesc d{};
+  d.kind = iris::OP_RS;
+  d.C = C;
+  d.out = out;
+  d.A = A;
+  d.srcs = partials;
+  d.W = W;
+  d.rank = rank;
+  d.B = B;
+  d.bias = bias;
+  d.M = M;
+  d.N = N;
+  d.K = K;
+  return run(d, cfg, workspace, workspace_bytes, stream);
+}
+
+int iris_mm_ar_local(void* out, void* C, const void* A, const void* B, const void* bias,
+                     const void* const* partials, int32_t W, int64_t M, int64_t N, int64_t K,
+                     const iris_config_t* cfg, void* workspace, size_t workspace_bytes, void* stream) {
+  g_msg.clear();
+  if (W < 1 || W > IRIS_MAX_W) return fail(IRIS_ERR_INVALID_ARG, "W must be in [1, %d] (got %d)", IRIS_MAX_W, W);
+  int st;
+  if ((st = check_ptr(out, "out")) || (st = check_ptr(C, "C")) || (st = check_ptr(A, "A")) ||
+      (st = check_ptr(B, "B")) || (st = check_ptr(bias, "bias", false)) || (st = copy_ptrs(partials, W - 1, "partials")))
+    return st;
+  if ((st = check_gemm_dims(M, N, K))) return st;
+  OpDesc d{};
+  d.kind = iris::OP_ARMM;
+  d.C = C;
+  d.out = out;
+  d.A = A;
+  d.srcs = partials;
+  d.W = W;
+  d.B = B;
+  d.bias = bias;
+  d.M = M;
+  d.N = N;
+  d.K = K;
+  return run(d, cfg, workspace, workspace_bytes, stream);
+}
+
+int iris_concurrent(void* C, const void* A, const void* B, const void* bias, int64_t M, int64_t N, int64_t K,
+                    int32_t collective, void* comm_out, const void* const* comm_in, int32_t W,
+                    int64_t comm_elems, const iris_config_t* cfg, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  g_msg.clear();
+  if (collective != IRIS_COLL_ALL_REDUCE)
+    return fail(IRIS_ERR_UNSUPPORTED, "collective %d is not supported (only IRIS_COLL_ALL_REDUCE)", collective);
+  if (W < 1 || W > IRIS_MAX_W) return fail(IRIS_ERR_INVALID_ARG, "W must be in [1, %d] (got %d)", IRIS_MAX_W, W);
+  int st;
+  if ((st = check_ptr(C, "C")) || (st = check_ptr(A, "A")) || (st = check_ptr(B, "B")) ||
+      (st = check_ptr(bias, "bias", false)) || (st = check_ptr(comm_out, "comm_out")) ||
+      (st = copy_ptrs(comm_in, W, "comm_in")))
+    return st;
+  if ((st = check_gemm_dims(M, N, K))) return st;
+  if (comm_elems <= 0) return fail(IRIS_ERR_INVALID_ARG, "comm_elems must be positive");
+  if (comm_elems % 8 != 0) return fail(IRIS_ERR_ALIGNMENT, "comm_elems must be a multiple of 8");
+  if (comm_elems > ((int64_t)1 << 40)) return fail(IRIS_ERR_UNSUPPORTED, "comm_elems too large");
+  OpDesc d{};
+  d.kind = iris::OP_CONC_AR;
+  d.C = C;
+  d.out = comm_out;
+  d.A = A;
+  d.srcs = comm_in;
+  d.W = W;
+  d.B = B;
+  d.bias = bias;
+  d.M = M;
+  d.N = N;
+  d.K = K;
+  d.comm_elems = comm_elems;
+  return run(d, cfg, workspace, workspace_bytes, stream);
+}
+
+size_t iris_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32_t W, const iris_config_t* cfg) {
+  (void)K;
+  Resolved r{};
+  if (resolve_static(cfg, &r)) return 0;
+  const int kind = iris_op_to_kind(op);
+  if (kind < 0 || M <= 0 || N <= 0 || W < 1 || W > IRIS_MAX_W) return 0;
+  return int_region_bytes(flag_words(kind, M, N, W, r.bm, r.bn)) + kStampBytes;
+}
+
+int iris_grid_size(const iris_config_t* cfg) {
+  Resolved r{};
+  int st = resolve_static(cfg, &r);
+  if (st) return -st;
+  int dev;
+  DevInfo di;
+  st = current_device(&dev, &di);
+  if (st) return -st;
+  const int occ = iris::persistent_blocks_per_cu(r.bm, r.bn, iris::OP_AG);
+  if (occ <= 0) return -fail(IRIS_ERR_HIP, "occupancy query failed");
+  return std::min(di.cus * occ, kMaxGrid);
+}
+
+int iris_tune_gemm_wgs(const iris_op_args_t* a, const int32_t* candidates, int32_t n_candidates, int32_t reps,
+                       int32_t* best_gemm_wgs, float* ms_out, void* stream) {
+  g_msg.clear();
+  if (!a || !best_gemm_wgs) return fail(IRIS_ERR_INVALID_ARG, "args and best_gemm_wgs must not be NULL");
+  if (n_candidates < 0 || (n_candidates > 0 && !candidates))
+    return fail(IRIS_ERR_INVALID_ARG, "bad candidate list");
+  if (reps < 1) reps = 5;
+  iris_config_t cfg = a->cfg;
+  cfg.mode = IRIS_MODE_FUSED;
+  // the static default is always benchmarked, so tuning never loses to it
+  int G = iris_grid_size(&cfg);
+  if (G < 0) return -G;
+  std::vector<int> cands(candidates, candidates + n_candidates);
+  const int def = (G * 7) / 8;
+  if (std::find(cands.begin(), cands.end(), def) == cands.end()) cands.push_back(def);
+  auto call = [&](int gw) -> int {
+    cfg.gemm_wgs = gw;
+    switch (a->op) {
+      case IRIS_OP_AG_MM:
+        return iris_ag_mm(a->C, a->out, a->srcs, a->W, a->B, a->bias, a->M, a->N, a->K, &cfg, nullptr, 0, stream);
+      case IRIS_OP_MM_RS:
+        return iris_mm_rs_local(a->out, a->C, a->A, a->B, a->bias, a->srcs, a->W, a->rank, a->M, a->N, a->K, &cfg,
+                                nullptr, 0, stream);
+      case IRIS_OP_MM_AR:
+        return iris_mm_ar_local(a->out, a->C, a->A, a->B, a->bias, a->srcs, a->W, a->M, a->N, a->K, &cfg, nullptr,
+                                0, stream);
+      case IRIS_OP_CONCURRENT:
+        return iris_concurrent(a->C, a->A, a->B, a->bias, a->M, a->N, a->K, IRIS_COLL_ALL_REDUCE, a->out, a->srcs,
+                               a->W, a->comm_elems, &cfg, nullptr, 0, stream);
+    }
+    return fail(IRIS_ERR_INVALID_ARG, "unknown op %d", a->op);
+  };
+  hipEvent_t e0, e1;
+  hipError_t he = hipEventCreate(&e0);
+  if (he != hipSuccess) return hip_fail(he, "hipEventCreate");
+  he = hipEventCreate(&e1);
+  if (he != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return hip_fail(he, "hipEventCreate");
+  }
+  const hipStream_t s = (hipStream_t)stream;
+  int best = -1;
+  float best_ms = 0;
+  int status = IRIS_OK;
+  for (size_t i = 0; i < cands.size() && status == IRIS_OK; ++i) {
+    const int gw = cands[i];
+    for (int w = 0; w < 2 && status == IRIS_OK; ++w) status = call(gw);
+    std::vector<float> t;
+    for (int r = 0; r < reps && status == IRIS_OK; ++r) {
+      he = hipEventRecord(e0, s);
+      if (he != hipSuccess) { status = hip_fail(he, "hipEventRecord"); break; }
+      status = call(gw);
+      he = hipEventRecord(e1, s);
+      if (he != hipSuccess) { status = hip_fail(he, "hipEventRecord"); break; }
+      if (status) break;
+      he = hipEventSynchronize(e1);
+      if (he != hipSuccess) {
+        status = hip_fail(he, "hipEventSynchronize");
+        break;
+      }
+      float ms = 0;
+      (void)hipEventElapsedTime(&ms, e0, e1);
+      t.push_back(ms);
+    }
+    if (status) break;
+    std::sort(t.begin(), t.end());
+    const float med = t[t.size() / 2];
+    if (ms_out && (int)i < n_candidates) ms_out[i] = med;
+    if (best < 0 || med < best_ms || (med == best_ms && gw > best)) {
+      best = gw;
+      best_ms = med;
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (status) return status;
+  *best_gemm_wgs = best;
+  int dev;
+  DevInfo di;
+  if (current_device(&dev, &di) == IRIS_OK) {
+    Resolved r{};
+    resolve_static(&cfg, &r);
+    // AG keys on K_local (args->K), the other ops on K, as run() looks them up
+    save_cache_entry(cache_key(di.arch, a->op, a->M, a->N, a->K, a->W, r.bm, r.bn, r.bk, r.gm), best);
+  }
+  return IRIS_OK;
+}
+
+int iris_last_windows(void* workspace, void* stream, double* gs_ns, double* ge_ns, double* cs_ns, double* ce_ns) {
+  g_msg.clear();
+  void* ws = workspace;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  LastLaunch last;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!ws) {
+      auto it = g_ws.find({dev, stream});
+      if (it == g_ws.end()) return fail(IRIS_ERR_INVALID_ARG, "no library workspace for this stream yet");
+      ws = it->second.ptr;
+    }
+    auto lt = g_last.find(ws);
+    if (lt == g_last.end()) return fail(IRIS_ERR_INVALID_ARG, "no launch recorded for this workspace");
+    last = lt->second;
+  }
+  if (!last.fused) return fail(IRIS_ERR_INVALID_ARG, "the last launch on this workspace was not fused");
+  e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  std::vector<uint64_t> st((size_t)last.grid * 4);
+  e = hipMemcpy(st.data(), (char*)ws + last.stamp_off, st.size() * 8, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "stamp readback");
+  DevInfo di;
+  int d2;
+  int s2 = current_device(&d2, &di);
+  if (s2) return s2;
+  uint64_t lo = ~0ull, gs = ~0ull, ge = 0, cs = ~0ull, ce = 0;
+  for (int b = 0; b < last.grid; ++b) {
+    const uint64_t* w = &st[(size_t)b * 4];
+    if (w[1]) { gs = std::min(gs, w[0]); ge = std::max(ge, w[1]); }
+    if (w[3]) { cs = std::min(cs, w[2]); ce = std::max(ce, w[3]); }
+  }
+  lo = std::min(gs, cs);
+  const double ns_per_tick = 1e6 / (double)di.wall_khz;
+  auto conv = [&](uint64_t v) { return (v == ~0ull || v == 0) ? -1.0 : (double)(v - lo) * ns_per_tick; };
+  if (gs_ns) *gs_ns = conv(gs);
+  if (ge_ns) *ge_ns = conv(ge);
+  if (cs_ns) *cs_ns = conv(cs);
+  if (ce_ns) *ce_ns = conv(ce);
+  return IRIS_OK;
+}
+
+int iris_device_info(int32_t device, iris_device_info_t* info) {
+  g_msg.clear();
+  if (!info) return fail(IRIS_ERR_INVALID_ARG, "info is NULL");
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess || n == 0) return fail(IRIS_ERR_NO_DEVICE, "no HIP device");
+  if (device < 0 || device >= n) return fail(IRIS_ERR_INVALID_ARG, "device %d out of range", device);
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, device);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  memset(info, 0, sizeof *info);
+  info->device = device;
+  info->compute_units = prop.multiProcessorCount;
+  info->clock_khz = prop.clockRate;
+  info->memory_clock_khz = prop.memoryClockRate;
+  info->lds_bytes_per_cu = (int32_t)prop.maxSharedMemoryPerMultiProcessor;
+  info->global_mem_bytes = (int64_t)prop.totalGlobalMem;
+  snprintf(info->arch, sizeof info->arch, "%s", prop.gcnArchName);
+  return IRIS_OK;
+}
+
+const char* iris_status_str(int32_t s) {
+  switch (s) {
+    case IRIS_OK: return "IRIS_OK";
+    case IRIS_ERR_INVALID_ARG: return "IRIS_ERR_INVALID_ARG";
+    case IRIS_ERR_UNSUPPORTED: return "IRIS_ERR_UNSUPPORTED";
+    case IRIS_ERR_CONFIG: return "IRIS_ERR_CONFIG";
+    case IRIS_ERR_ALIGNMENT: return "IRIS_ERR_ALIGNMENT";
+    case IRIS_ERR_NO_MEMORY: return "IRIS_ERR_NO_MEMORY";
+    case IRIS_ERR_HIP: return "IRIS_ERR_HIP";
+    case IRIS_ERR_WORKSPACE: return "IRIS_ERR_WORKSPACE";
+    case IRIS_ERR_NO_DEVICE: return "IRIS_ERR_NO_DEVICE";
+    case IRIS_ERR_DEVICE_TIMEOUT: return "IRIS_ERR_DEVICE_TIMEOUT";
+  }
+  return "IRIS_ERR_UNKNOWN";
+}
+
+const char* iris_last_error_message(void) { return g_msg.c_str(); }
+
+int iris_finalize(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  int status = IRIS_OK;
+  for (auto& kv : g_ws) {
+    if (kv.second.ptr) {
+      (void)hipSetDevice(kv.first.first);
+      (void)hipStreamSynchronize((hipStream_t)kv.first.second);
+      if (hipFree(kv.second.ptr) != hipSuccess) status = IRIS_ERR_HIP;
+    }
+  }
+  g_ws.clear();
+  g_last.clear();
+  return status;
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Host-side view of the persistent kernels: the parameter block every launch
+// takes and the launch entry points implemented in kernels.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "comm_units.hpp"
+#include "gemm_tile.hpp"
+
+namespace iris {
+
+enum OpKind : int32_t {
+  OP_GEMM = 0,        // GEMM queue only (no comm units)
+  OP_AG = 1,          // comm: all_gather copy units; GEMM waits on row flags
+  OP_RS = 2,          // comm: reduce_scatter units wait on GEMM tile flags
+  OP_ARMM = 3,        // comm: matmul_all_reduce units wait on GEMM tile flags
+  OP_CONC_AR = 4,     // comm: independent flat all_reduce units
+};
+
+// Workspace layout (int32 words):
+//   [0] GEMM queue counter   [1] comm queue counter   [2] error word
+//   [3] reserved             [kFlagBase ...] ready flags
+// followed (64-byte aligned) by uint64 stamps[G][4].
+constexpr int kCtrGemm = 0, kCtrComm = 1, kErr = 2;
+constexpr int kFlagBase = 16;
+
+struct Params {
+  GemmArgs g;
+  CommArgs c;
+  int32_t op;
+  int32_t n_pm, n_pn, group_m;
+  int32_t prio_lo, prio_hi;  // GEMM column tiles [prio_lo, prio_hi) go first
+  int32_t T_gemm, T_comm;
+  int32_t gemm_wgs;          // pid < gemm_wgs starts on the GEMM queue
+  int32_t steal;             // switch to the other queue when the first is empty
+  int32_t fused;             // 1: flags are produced and awaited in this launch
+  int32_t* ws;               // counters + flags
+  uint64_t* stamps;          // [gridDim.x][4]: gemm start/end, comm start/end
+  uint32_t spin_limit;       // bound on polls of one flag wait
+};
+
+hipError_t launch_persistent(const Params& p, int bm, int bn, int grid, hipStream_t s);
+hipError_t launch_comm_only(const Params& p, int grid, hipStream_t s);
+hipError_t launch_reset(int32_t* ws, int n_words, hipStream_t s);
+// workgroups of the persistent kernel resident per CU, or <= 0 on error
+int persistent_blocks_per_cu(int bm, int bn, int op);
+bool tile_supported(int bm, int bn);
+
+}  // namespace iris

@@ -1,0 +1,254 @@
+/*
+ * iris_local: one GPU's share of Iris-style fused communication + GEMM ops
+ * on AMD Instinct MI355X (gfx950). C ABI.
+ *
+ * Sources of the operation definitions:
+ *   [DOCS]   Iris docs, "Fused Communication and Compute Operations":
+ *            entries all_gather_matmul, matmul_reduce_scatter,
+ *            matmul_all_reduce (signatures: output, inputs, optional bias of
+ *            length M or N, optional FusedConfig, optional workspace).
+ *   [PR544]  ROCm/iris PR "Add iris.concurrent (concurrent, independent,
+ *            fused comm+gemm)": description (persistent work-stealing
+ *            kernels, the GEMM/comm split `gemm_wgs` and the GEMM tile are
+ *            the knobs; fused = one persistent kernel with two work-stealing
+ *            queues) and review answer (the GEMM and the collective are
+ *            independent).
+ *   [PR506]  ROCm/iris PR "Add auto-config selection for fused AG+matmul
+ *            with 28 tuned HBM buffer configs": summary (config=None selects
+ *            a configuration automatically; only the NN layout is supported).
+ *
+ * One GPU's share: the other ranks' shards and partial buffers are stand-in
+ * buffers already resident in this GPU's memory, passed by pointer. There is
+ * no communication between GPUs here.
+ *
+ * Data conventions (all entry points):
+ *   - fp16 is IEEE binary16, stored as 2-byte elements.
+ *   - Matrices are row-major and contiguous (the NN layout of [PR506]).
+ *   - Every matrix and vector pointer is a DEVICE pointer, 16-byte aligned.
+ *     Pointer ARRAYS (A_shards, partials, comm_in) are HOST arrays of device
+ *     pointers; the library copies them before returning.
+ *   - Row lengths must be multiples of 8 elements (16 bytes): K_local (or K)
+ *     and N for the GEMM, N/W for reduce_scatter.
+ *   - Outputs must not overlap inputs.
+ *   - bias may be NULL. It has N entries (added to every row), or M entries
+ *     (added to every column) when IRIS_FLAG_BIAS_ALONG_M is set.
+ *   - Accumulation is fp32; every fp16 output is rounded once, to nearest
+ *     even.
+ *
+ * Ownership: the caller owns every buffer. The library keeps no caller
+ * pointer after the work it enqueued has run. If `workspace` is NULL the
+ * library uses a workspace of its own per (device, stream), allocated on
+ * first use and released by iris_finalize().
+ *
+ * Synchronisation: every op only enqueues work on `stream` (a hipStream_t
+ * passed as void*; NULL is the default stream) and returns without waiting.
+ * Two calls that share one workspace must not run concurrently.
+ *
+ * Errors: every function returns an iris_status (0 = IRIS_OK). Arguments are
+ * validated before any HIP call; on error nothing is enqueued. A
+ * human-readable message for the last error on the calling thread is
+ * returned by iris_last_error_message().
+ */
+#ifndef IRIS_LOCAL_H
+#define IRIS_LOCAL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define IRIS_MAX_W 16
+
+typedef enum iris_status {
+  IRIS_OK = 0,
+  IRIS_ERR_INVALID_ARG = 1,   /* NULL pointer, bad size, W out of range, ... */
+  IRIS_ERR_UNSUPPORTED = 2,   /* a valid request this build does not serve */
+  IRIS_ERR_CONFIG = 3,        /* tile shape / gemm_wgs / mode not allowed */
+  IRIS_ERR_ALIGNMENT = 4,     /* pointer not 16-byte aligned or row length % 8 */
+  IRIS_ERR_NO_MEMORY = 5,     /* internal workspace allocation failed */
+  IRIS_ERR_HIP = 6,           /* a HIP runtime call failed (message has it) */
+  IRIS_ERR_WORKSPACE = 7,     /* caller workspace smaller than required */
+  IRIS_ERR_NO_DEVICE = 8,     /* no usable gfx950 device */
+  IRIS_ERR_DEVICE_TIMEOUT = 9 /* a bounded device-side wait expired */
+} iris_status;
+
+/* execution modes ([PR544] description) */
+#define IRIS_MODE_FUSED 0      /* one persistent kernel, two work queues */
+#define IRIS_MODE_SEQUENTIAL 1 /* comm kernel and GEMM kernel, one after the
+                                  other on the same stream, each on the whole
+                                  GPU (the unfused baseline) */
+
+/* config flags */
+#define IRIS_FLAG_NO_STEAL 1     /* workgroups stay on their first queue */
+#define IRIS_FLAG_BIAS_ALONG_M 2 /* bias has M entries instead of N */
+
+/* op ids (workspace sizing, tuning) */
+#define IRIS_OP_AG_MM 1
+#define IRIS_OP_MM_RS 2
+#define IRIS_OP_MM_AR 3
+#define IRIS_OP_CONCURRENT 4
+
+/* collectives for iris_concurrent */
+#define IRIS_COLL_ALL_REDUCE 1
+
+/*
+ * Tuning knobs ([PR544]: the GEMM/comm split gemm_wgs and the GEMM tile;
+ * [DOCS]: FusedConfig). A field <= 0 means "choose automatically": the
+ * tuned value cached for this shape if there is one (iris_tune_gemm_wgs),
+ * else the built-in default. Passing NULL means all fields automatic.
+ *   block_m, block_n  GEMM output tile; supported pairs: 256x256, 256x128,
+ *                     128x128, 64x64. Default 256x256.
+ *   block_k           K step; 64 only. Default 64.
+ *   group_m           rows of tiles per swizzle group. Default 8.
+ *   gemm_wgs          workgroups that start on the GEMM queue in fused mode,
+ *                     1..G-1 where G = iris_grid_size(). Default 7/8 of G.
+ *   comm_block_n      columns per reduce unit (reduce_scatter and
+ *                     matmul_all_reduce), multiple of 8. Default block_n.
+ *   comm_chunk        elements per all_reduce unit of iris_concurrent,
+ *                     multiple of 2048. Default 65536.
+ *   mode              IRIS_MODE_FUSED (default) or IRIS_MODE_SEQUENTIAL.
+ *   flags             IRIS_FLAG_* bits.
+ */
+typedef struct iris_config {
+  int32_t block_m;
+  int32_t block_n;
+  int32_t block_k;
+  int32_t group_m;
+  int32_t gemm_wgs;
+  int32_t comm_block_n;
+  int32_t comm_chunk;
+  int32_t mode;
+  int32_t flags;
+} iris_config_t;
+
+/*
+ * all_gather_matmul, local share ([DOCS] all_gather_matmul):
+ *   A_gathered[m][s*K_local + k] = A_shards[s][m][k]       (bit copy)
+ *   C = A_gathered @ B + bias
+ * C: (M, N) fp16 out. A_gathered: (M, W*K_local) fp16 out, the gathered
+ * buffer the GEMM reads. A_shards: host array of W device pointers, each
+ * (M, K_local) fp16, in rank order. B: (W*K_local, N) fp16. bias: N (or M).
+ * In fused mode comm workgroups copy the shards while GEMM workgroups
+ * compute; a GEMM tile starts on row block pm once every shard of that row
+ * block has landed.
+ */
+int iris_ag_mm(void* C, void* A_gathered, const void* const* A_shards, int32_t W,
+               const void* B, const void* bias, int64_t M, int64_t N,
+               int64_t K_local, const iris_config_t* cfg, void* workspace,
+               size_t workspace_bytes, void* stream);
+
+/*
+ * matmul_reduce_scatter, local share for rank `rank` of W
+ * ([DOCS] matmul_reduce_scatter, along N):
+ *   C = A @ B + bias                                         (M, N)
+ *   out[m][j] = C[m][rank*N/W + j] + sum_{p<W-1} partials[p][m][j]
+ * out: (M, N/W) fp16 out. C: (M, N) fp16 out (this rank's full partial
+ * product; the reduction reads its own slice back from C). partials: host
+ * array of W-1 device pointers, each (M, N/W) fp16, standing in for the
+ * other ranks' slices. Requires N % W == 0 and (N/W) % 8 == 0.
+ */
+int iris_mm_rs_local(void* out, void* C, const void* A, const void* B,
+                     const void* bias, const void* const* partials, int32_t W,
+                     int32_t rank, int64_t M, int64_t N, int64_t K,
+                     const iris_config_t* cfg, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * matmul_all_reduce, local share ([DOCS] matmul_all_reduce):
+ *   C = A @ B + bias;  out = C + sum_{p<W-1} partials[p]          (M, N)
+ * partials: host array of W-1 device pointers, each (M, N) fp16.
+ */
+int iris_mm_ar_local(void* out, void* C, const void* A, const void* B,
+                     const void* bias, const void* const* partials, int32_t W,
+                     int64_t M, int64_t N, int64_t K, const iris_config_t* cfg,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Independent GEMM beside a collective ([PR544]):
+ *   C = A @ B + bias                                (M, N), and independently
+ *   comm_out[i] = sum_{w<W} comm_in[w][i]           (all_reduce, comm_elems)
+ * collective must be IRIS_COLL_ALL_REDUCE (others: IRIS_ERR_UNSUPPORTED).
+ * comm_in: host array of W device pointers, each comm_elems fp16;
+ * comm_elems % 8 == 0.
+ */
+int iris_concurrent(void* C, const void* A, const void* B, const void* bias,
+                    int64_t M, int64_t N, int64_t K, int32_t collective,
+                    void* comm_out, const void* const* comm_in, int32_t W,
+                    int64_t comm_elems, const iris_config_t* cfg,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace an op needs (0 on invalid arguments). The
+ * workspace holds the two queue counters, the ready flags and per-workgroup
+ * timestamps; callers passing their own must give at least this much. */
+size_t iris_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32_t W,
+                           const iris_config_t* cfg);
+
+/* Persistent grid size G (workgroups) the fused kernels launch on the
+ * current device for this config, or a negative iris_status. */
+int iris_grid_size(const iris_config_t* cfg);
+
+/*
+ * Host-side CU-split sweep ([PR544]: benchmark candidates, always including
+ * the static default, cache the winner). Runs the op described by `args`
+ * in fused mode once per candidate gemm_wgs (warmup + `reps` timed runs,
+ * median), writes the winner to *best_gemm_wgs and the median milliseconds
+ * of each candidate to ms_out[i] (may be NULL), and stores the winner in the
+ * tuning cache (file named by IRIS_LOCAL_TUNE_CACHE, default
+ * ~/.cache/iris_local/tune.txt; written to a temporary file then renamed;
+ * a failed write is ignored). Blocks until done. Ties go to more GEMM
+ * workgroups. The op's outputs hold the last candidate's results.
+ */
+typedef struct iris_op_args {
+  int32_t op;             /* IRIS_OP_* */
+  void* C;
+  void* out;              /* A_gathered (AG), out (RS/AR), comm_out (concurrent) */
+  const void* A;          /* A (RS/AR/concurrent); unused for AG */
+  const void* const* srcs;/* A_shards (AG), partials (RS/AR), comm_in */
+  int32_t W;
+  int32_t rank;           /* RS only */
+  const void* B;
+  const void* bias;
+  int64_t M, N, K;        /* K is K_local for AG */
+  int64_t comm_elems;     /* concurrent only */
+  iris_config_t cfg;      /* gemm_wgs is overridden by each candidate */
+} iris_op_args_t;
+
+int iris_tune_gemm_wgs(const iris_op_args_t* args, const int32_t* candidates,
+                       int32_t n_candidates, int32_t reps, int32_t* best_gemm_wgs,
+                       float* ms_out, void* stream);
+
+/*
+ * Per-workgroup timestamps of the last fused launch that used `workspace`
+ * (or the library's own workspace for `stream` if workspace is NULL), in
+ * nanoseconds since the earliest stamp: the windows in which GEMM tiles and
+ * comm units ran. Waits for `stream`. Any output may be NULL.
+ */
+int iris_last_windows(void* workspace, void* stream, double* gemm_start_ns,
+                      double* gemm_end_ns, double* comm_start_ns,
+                      double* comm_end_ns);
+
+typedef struct iris_device_info {
+  int32_t device;
+  int32_t compute_units;
+  int32_t clock_khz;         /* max engine clock */
+  int32_t memory_clock_khz;
+  int32_t lds_bytes_per_cu;
+  int64_t global_mem_bytes;
+  char arch[64];             /* gcnArchName, e.g. "gfx950:sramecc+:xnack-" */
+} iris_device_info_t;
+
+int iris_device_info(int32_t device, iris_device_info_t* info);
+
+const char* iris_status_str(int32_t status);
+/* Message for the last error on this thread ("" if none). */
+const char* iris_last_error_message(void);
+/* Frees the library's own workspaces. */
+int iris_finalize(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IRIS_LOCAL_H */

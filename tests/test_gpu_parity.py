@@ -1,0 +1,275 @@
+"""Parity of the HIP path (through the C-ABI) with the CPU oracle, on small
+and ragged shapes that span several tiles, plus the invariants that pin the
+schedule: bit-identical results across gemm_wgs, modes and repeats.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_util import assert_bits_equal, assert_close, assert_exact, empty, host, note
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import gemm_collective_tile_amd as il
+    from gemm_collective_tile_amd import Config
+else:  # collected on a CPU-only host; every test here is marked gpu
+    il = None
+    Config = None
+
+TILES = [(64, 64), (128, 128), (256, 128), (256, 256)]
+
+
+def cuda(xs):
+    if xs is None:
+        return None
+    if isinstance(xs, list):
+        return [x.cuda() for x in xs]
+    return xs.cuda()
+
+
+def ag_inputs(M, N, kl, W, seed=0, integer=False, bias=True, along_m=False):
+    w = wl.Workload("case", "ag_mm", M=M, N=N, K=kl * W, W=W, a_std=1.0, b_std=(kl * W) ** -0.5)
+    inp = wl.make_inputs(w, seed=seed, integer=integer, with_bias=bias, bias_along_m=along_m)
+    return inp
+
+
+def run_ag(inp, cfg=None):
+    shards, B, bias = cuda(inp["shards"]), cuda(inp["B"]), cuda(inp["bias"])
+    M, kl = shards[0].shape
+    C = empty((M, B.shape[1]))
+    G = empty((M, kl * len(shards)))
+    il.iris_ag_mm(C, G, shards, B, bias, config=cfg)
+    torch.cuda.synchronize()
+    return C, G
+
+
+def oracle_ag(inp, along_m=False):
+    sh = [host(s) for s in inp["shards"]]
+    bias = None if inp["bias"] is None else host(inp["bias"])
+    return (oracle.all_gather_k(sh).view(np.float16),
+            oracle.all_gather_matmul(sh, host(inp["B"]), bias, bias_along_m=along_m))
+
+
+# ------------------------------------------------------------ all_gather + MM
+
+def test_tiny_workload_all_configs():
+    """The tiny workload (W=2, 256x256 shards) under every tile and schedule."""
+    w = wl.WORKLOADS["tiny"]
+    inp = wl.make_inputs(w, seed=0)
+    g_ref, c_ref = oracle_ag(inp)
+    G = il.iris_grid_size(Config(block_m=64, block_n=64))
+    cfgs = [None] + [Config(block_m=bm, block_n=bn) for bm, bn in TILES] + [
+        Config(block_m=64, block_n=64, mode=il.IRIS_MODE_SEQUENTIAL),
+        Config(block_m=64, block_n=64, gemm_wgs=1),
+        Config(block_m=64, block_n=64, gemm_wgs=G - 1),
+        Config(block_m=64, block_n=64, flags=il.IRIS_FLAG_NO_STEAL),
+        Config(block_m=64, block_n=64, group_m=1),
+    ]
+    first64 = None
+    for cfg in cfgs:
+        note(f"tiny ag_mm cfg={cfg}")
+        C, Gb = run_ag(inp, cfg)
+        assert_bits_equal(Gb, g_ref, f"gathered {cfg}")
+        assert_close(C, c_ref, f"C {cfg}")
+        if cfg is not None and cfg.block_m == 64:
+            if first64 is None:
+                first64 = C
+            else:
+                assert_bits_equal(C, first64, f"schedule invariance {cfg}")
+
+
+@pytest.mark.parametrize("M,N,kl,W", [(256, 256, 256, 2), (300, 200, 40, 3), (64, 72, 8, 1)])
+@pytest.mark.parametrize("tile", TILES)
+def test_ag_mm_integer_exact(M, N, kl, W, tile):
+    inp = ag_inputs(M, N, kl, W, seed=1, integer=True)
+    g_ref, c_ref = oracle_ag(inp)
+    note(f"integer ag_mm M={M} N={N} kl={kl} W={W} tile={tile}")
+    C, Gb = run_ag(inp, Config(block_m=tile[0], block_n=tile[1]))
+    assert_bits_equal(Gb, g_ref, "gathered")
+    assert_exact(C, c_ref, "C")
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_ag_mm_ragged(tile):
+    """M, N, K all off the tile grid (K = 120 is not a multiple of 64)."""
+    inp = ag_inputs(300, 200, 40, 3, seed=2)
+    g_ref, c_ref = oracle_ag(inp)
+    note(f"ragged ag_mm tile={tile}")
+    C, Gb = run_ag(inp, Config(block_m=tile[0], block_n=tile[1]))
+    assert_bits_equal(Gb, g_ref, "gathered")
+    assert_close(C, c_ref, "C")
+
+
+def test_ag_mm_bias_variants():
+    for bias, along_m in [(False, False), (True, True)]:
+        inp = ag_inputs(192, 320, 64, 2, seed=3, bias=bias, along_m=along_m)
+        g_ref, c_ref = oracle_ag(inp, along_m=along_m)
+        flags = il.IRIS_FLAG_BIAS_ALONG_M if along_m else 0
+        for tile in [(64, 64), (256, 256)]:
+            note(f"ag_mm bias={bias} along_m={along_m} tile={tile}")
+            C, Gb = run_ag(inp, Config(block_m=tile[0], block_n=tile[1], flags=flags))
+            assert_close(C, c_ref, f"C bias={bias} along_m={along_m}")
+
+
+def test_ag_w1_equals_plain_gemm():
+    """W = 1: all_gather_matmul is a plain GEMM, bit-for-bit the GEMM of the
+    concurrent op on the same operands."""
+    inp = ag_inputs(320, 256, 192, 1, seed=4)
+    _, c_ref = oracle_ag(inp)
+    C, _ = run_ag(inp, Config(block_m=128, block_n=128))
+    A = cuda(inp["shards"][0])
+    C2 = empty((320, 256))
+    xs = [torch.zeros(2048, dtype=torch.float16, device="cuda")]
+    out = empty((2048,))
+    il.iris_concurrent(C2, A, cuda(inp["B"]), out, xs, bias=cuda(inp["bias"]),
+                       config=Config(block_m=128, block_n=128))
+    torch.cuda.synchronize()
+    assert_close(C, c_ref, "C")
+    assert_bits_equal(C, C2, "W=1 all_gather_matmul vs plain GEMM")
+
+
+# ----------------------------------------------------------- reduce_scatter
+
+def rs_inputs(M, N, K, W, seed=0, integer=False, zero_partials=False):
+    w = wl.Workload("case", "mm_rs", M=M, N=N, K=K, W=W, a_std=K ** -0.25, b_std=K ** -0.25)
+    inp = wl.make_inputs(w, seed=seed, integer=integer)
+    if zero_partials:
+        inp["partials"] = [torch.zeros_like(p) for p in inp["partials"]]
+    return inp
+
+
+def run_rs(inp, W, rank, cfg=None):
+    A, B, bias, parts = cuda(inp["A"]), cuda(inp["B"]), cuda(inp["bias"]), cuda(inp["partials"])
+    M, N = A.shape[0], B.shape[1]
+    C = empty((M, N))
+    out = empty((M, N // W))
+    il.iris_mm_rs_local(out, C, A, B, parts, W, rank=rank, bias=bias, config=cfg)
+    torch.cuda.synchronize()
+    return out, C
+
+
+@pytest.mark.parametrize("rank", [0, 3])
+@pytest.mark.parametrize("tile", TILES)
+def test_mm_rs_small(rank, tile):
+    W, M, N, K = 4, 300, 800, 136
+    inp = rs_inputs(M, N, K, W, seed=5)
+    ref = oracle.matmul_reduce_scatter(host(inp["A"]), host(inp["B"]), [host(p) for p in inp["partials"]],
+                                       W, rank=rank, bias=host(inp["bias"]))
+    cref = oracle.gemm_bias(host(inp["A"]), host(inp["B"]), host(inp["bias"]))
+    outs = []
+    for mode in (il.IRIS_MODE_FUSED, il.IRIS_MODE_SEQUENTIAL):
+        note(f"mm_rs rank={rank} tile={tile} mode={mode}")
+        out, C = run_rs(inp, W, rank, Config(block_m=tile[0], block_n=tile[1], mode=mode, comm_block_n=64))
+        assert_close(C, cref, "C")
+        assert_close(out, ref, "out")
+        outs.append(out)
+    assert_bits_equal(outs[0], outs[1], "fused vs sequential")
+
+
+def test_mm_rs_integer_exact_and_zero_partials():
+    W, M, N, K = 8, 256, 1024, 512
+    inp = rs_inputs(M, N, K, W, seed=6, integer=True)
+    ref = oracle.matmul_reduce_scatter(host(inp["A"]), host(inp["B"]), [host(p) for p in inp["partials"]],
+                                       W, rank=5, bias=host(inp["bias"]))
+    out, _ = run_rs(inp, W, 5, Config(block_m=128, block_n=128))
+    assert_exact(out, ref, "integer-exact reduce_scatter")
+    z = rs_inputs(M, N, K, W, seed=7, zero_partials=True)
+    out, C = run_rs(z, W, 2)
+    assert_bits_equal(out, C[:, 2 * (N // W):3 * (N // W)].contiguous(), "zero partials -> own slice")
+
+
+def test_mm_rs_w1_and_partial_permutation():
+    inp = rs_inputs(128, 256, 64, 1, seed=8)
+    out, C = run_rs(inp, 1, 0)
+    assert_bits_equal(out, C, "W=1 reduce_scatter is the GEMM output")
+    inp = rs_inputs(256, 512, 128, 8, seed=9)
+    a, _ = run_rs(inp, 8, 1)
+    inp2 = dict(inp, partials=inp["partials"][::-1])
+    b, _ = run_rs(inp2, 8, 1)
+    ref = oracle.matmul_reduce_scatter(host(inp["A"]), host(inp["B"]), [host(p) for p in inp["partials"]],
+                                       8, rank=1, bias=host(inp["bias"]))
+    assert_close(a, ref, "partials in order")
+    assert_close(b, ref, "partials reversed")
+
+
+# -------------------------------------------------------- matmul_all_reduce
+
+@pytest.mark.parametrize("tile", [(64, 64), (256, 256)])
+def test_mm_ar_small(tile):
+    W, M, N, K = 3, 200, 320, 72
+    w = wl.Workload("case", "mm_ar", M=M, N=N, K=K, W=W, a_std=1.0, b_std=K ** -0.5)
+    inp = wl.make_inputs(w, seed=10)
+    A, B, bias, parts = cuda(inp["A"]), cuda(inp["B"]), cuda(inp["bias"]), cuda(inp["partials"])
+    ref = oracle.matmul_all_reduce(host(inp["A"]), host(inp["B"]), [host(p) for p in inp["partials"]], W,
+                                   bias=host(inp["bias"]))
+    for mode in (il.IRIS_MODE_FUSED, il.IRIS_MODE_SEQUENTIAL):
+        note(f"mm_ar tile={tile} mode={mode}")
+        C, out = empty((M, N)), empty((M, N))
+        il.iris_mm_ar_local(out, C, A, B, parts, W, bias=bias,
+                            config=Config(block_m=tile[0], block_n=tile[1], mode=mode))
+        torch.cuda.synchronize()
+        assert_close(out, ref, "out")
+
+
+# --------------------------------------------------------------- concurrent
+
+def test_concurrent_small_and_closed_forms():
+    M, N, K, W = 320, 256, 200, 8
+    n = 3 * 65536 + 8000  # ragged last unit
+    g = wl.Workload("case", "concurrent", M=M, N=N, K=K, W=W, a_std=1.0, b_std=K ** -0.5, comm_elems=n)
+    inp = wl.make_inputs(g, seed=11)
+    A, B, bias, xs = cuda(inp["A"]), cuda(inp["B"]), cuda(inp["bias"]), cuda(inp["comm_in"])
+    cref = oracle.gemm_bias(host(inp["A"]), host(inp["B"]), host(inp["bias"]))
+    aref = oracle.all_reduce([host(x) for x in inp["comm_in"]])
+    for cfg in [None, Config(block_m=64, block_n=64), Config(mode=il.IRIS_MODE_SEQUENTIAL),
+                Config(block_m=128, block_n=128, gemm_wgs=8)]:
+        note(f"concurrent cfg={cfg}")
+        C, out = empty((M, N)), empty((n,))
+        il.iris_concurrent(C, A, B, out, xs, bias=bias, config=cfg)
+        torch.cuda.synchronize()
+        assert_close(C, cref, "C")
+        assert_close(out, aref, "all_reduce")
+    # all-equal buffers: out = fp16(8 x), exact
+    x = xs[0]
+    out = empty((n,))
+    il.iris_concurrent(C, A, B, out, [x] * 8, bias=bias)
+    torch.cuda.synchronize()
+    assert_bits_equal(out, oracle.f16_encode(8 * host(x).astype(np.float64)).view(np.float16), "8 x")
+
+
+# ---------------------------------------------------- errors and bookkeeping
+
+def test_gpu_argument_errors():
+    inp = ag_inputs(256, 256, 64, 2)
+    G = il.iris_grid_size(None)
+    with pytest.raises(il.IrisError) as e:
+        run_ag(inp, Config(gemm_wgs=G))
+    assert e.value.status == 3
+    small = torch.empty(64, dtype=torch.uint8, device="cuda")
+    shards, B = cuda(inp["shards"]), cuda(inp["B"])
+    with pytest.raises(il.IrisError) as e:
+        il.iris_ag_mm(empty((256, 256)), empty((256, 128)), shards, B, None, workspace=small)
+    assert e.value.status == 7
+
+
+def test_windows_and_device_info():
+    info = il.iris_device_info(0)
+    note(f"device: {info}")
+    assert info["arch"].startswith("gfx950")
+    inp = ag_inputs(1024, 1024, 256, 4)
+    run_ag(inp)
+    gs, ge, cs, ce = il.iris_last_windows()
+    note(f"windows ns: gemm [{gs:.0f}, {ge:.0f}] comm [{cs:.0f}, {ce:.0f}]")
+    assert ge > gs >= 0 and ce > cs >= 0
+
+
+def test_repeat_runs_bit_identical():
+    inp = ag_inputs(512, 512, 128, 4, seed=12)
+    C0, G0 = run_ag(inp)
+    for i in range(5):
+        C, Gb = run_ag(inp)
+        assert_bits_equal(C, C0, f"repeat {i}")
+        assert_bits_equal(Gb, G0, f"repeat {i} gathered")
