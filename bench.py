@@ -1,0 +1,291 @@
+"""Benchmark of one GPU's share of the fused communication + GEMM ops on MI355X.
+
+One step = one call of the fused op on the headline workload (default
+pow2_4k all_gather_matmul: W=8 K-shards (4096, 512) gathered into (4096,
+4096) and multiplied by B (4096, 4096) plus bias), with every input already
+resident in HBM. The gemm_wgs split is swept first (untimed), as the host
+sweep does for any shape, then `--warmup` untimed and `--steps` timed steps
+run. Prints ONE JSON line.
+
+  value      GEMM TFLOP/s of the whole fused op: 2*M*N*K / (wall time per step)
+  roofline   the fused persistent kernel against the dense fp16 MFMA peak:
+             2*M*N*K / (average kernel duration from HIP events around each
+             launch on the op's stream)
+  comm       the communication units' HBM GB/s over their in-kernel window
+  cpu_baseline  the CPU oracle on the full headline problem (gather + GEMM +
+             bias in fp64) on the host's cores; also checks the GPU output
+  extra      the other workloads (llama7b_gate reduce_scatter, concurrent
+             8192^3 GEMM beside an all_reduce, g2 all_gather_matmul) measured
+             the same way, unless --headline-only
+
+Only one GPU is used: --gpus above 1 exits with a message.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="pow2_4k")
+    ap.add_argument("--headline-only", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for HBM counter scaling)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Case:
+    """Inputs, outputs and the step closure of one workload."""
+
+    def __init__(self, name):
+        import torch
+        import workloads as wl
+        import gemm_collective_tile_amd as il
+        self.il, self.torch = il, torch
+        self.w = w = wl.WORKLOADS[name]
+        self.inp = inp = wl.make_inputs(w, seed=0, device="cuda")
+        dev = dict(dtype=torch.float16, device="cuda")
+        if w.op == "ag_mm":
+            self.C = torch.empty(w.M, w.N, **dev)
+            self.G = torch.empty(w.M, w.K, **dev)
+            self.tune_kw = dict(C=self.C, out=self.G, srcs=inp["shards"], W=w.W, B=inp["B"],
+                                bias=inp["bias"], M=w.M, N=w.N, K=w.K_local)
+            self.op = il.IRIS_OP_AG_MM
+        elif w.op == "mm_rs":
+            self.C = torch.empty(w.M, w.N, **dev)
+            self.out = torch.empty(w.M, w.N_local, **dev)
+            self.tune_kw = dict(C=self.C, out=self.out, A=inp["A"], srcs=inp["partials"], W=w.W,
+                                rank=w.rank, B=inp["B"], bias=inp["bias"], M=w.M, N=w.N, K=w.K)
+            self.op = il.IRIS_OP_MM_RS
+        elif w.op == "concurrent":
+            self.C = torch.empty(w.M, w.N, **dev)
+            self.out = torch.empty(w.comm_elems, **dev)
+            self.tune_kw = dict(C=self.C, out=self.out, A=inp["A"], srcs=inp["comm_in"], W=w.W,
+                                B=inp["B"], bias=inp["bias"], M=w.M, N=w.N, K=w.K,
+                                comm_elems=w.comm_elems)
+            self.op = il.IRIS_OP_CONCURRENT
+        else:
+            raise ValueError(w.op)
+        self.G_wgs = il.iris_grid_size(None)
+
+    def step(self, cfg):
+        il, w, inp = self.il, self.w, self.inp
+        if w.op == "ag_mm":
+            il.iris_ag_mm(self.C, self.G, inp["shards"], inp["B"], inp["bias"], config=cfg)
+        elif w.op == "mm_rs":
+            il.iris_mm_rs_local(self.out, self.C, inp["A"], inp["B"], inp["partials"], w.W, rank=w.rank,
+                                bias=inp["bias"], config=cfg)
+        else:
+            il.iris_concurrent(self.C, inp["A"], inp["B"], self.out, inp["comm_in"], bias=inp["bias"],
+                               config=cfg)
+
+    def sweep_candidates(self):
+        G = self.G_wgs
+        fracs = [0.5, 0.75, 0.875]
+        if self.w.op == "concurrent":
+            fracs = [0.375, 0.5, 0.625, 0.75, 0.8125, 0.875, 0.9375]
+        return sorted({max(1, min(G - 1, int(math.floor(f * G)))) for f in fracs})
+
+
+def time_steps(case, cfg, steps, warmup):
+    """Wall time per step and the mean per-launch duration from HIP events."""
+    torch = case.torch
+    for _ in range(warmup):
+        case.step(cfg)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        case.step(cfg)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    dur = sorted(a.elapsed_time(b) for a, b in ev)
+    return wall_ms, sum(dur) / len(dur), dur[len(dur) // 2]
+
+
+def windows(case):
+    gs, ge, cs, ce = case.il.iris_last_windows()
+    g = (ge - gs) / 1e6 if ge >= 0 and gs >= 0 else None
+    c = (ce - cs) / 1e6 if ce >= 0 and cs >= 0 else None
+    return g, c
+
+
+def measure(name, steps, warmup, sweep):
+    il = __import__("gemm_collective_tile_amd")
+    case = Case(name)
+    w = case.w
+    Config = il.Config
+    best = None
+    sweep_ms = {}
+    if sweep:
+        cands = case.sweep_candidates()
+        log(f"[{name}] sweeping gemm_wgs over {cands}")
+        best, sweep_ms = il.iris_tune_gemm_wgs(case.op, cands, reps=5, **case.tune_kw)
+    cfg = Config(gemm_wgs=best or 0)
+    log(f"[{name}] timing fused mode, gemm_wgs={best}")
+    wall_ms, mean_ms, med_ms = time_steps(case, cfg, steps, warmup)
+    case.step(cfg)
+    gwin, cwin = windows(case)
+    log(f"[{name}] timing sequential mode")
+    seq_cfg = Config(mode=il.IRIS_MODE_SEQUENTIAL)
+    seq_wall, seq_mean, _ = time_steps(case, seq_cfg, max(3, steps // 2), 2)
+    case.step(seq_cfg)
+    sgwin, scwin = windows(case)
+    flops = w.gemm_flops
+    res = {
+        "workload": name, "op": w.op, "M": w.M, "N": w.N, "K": w.K, "W": w.W,
+        "gemm_wgs": best, "grid": case.G_wgs, "tile": "256x256x64",
+        "sweep_ms": {str(k): round(v, 4) for k, v in sweep_ms.items()},
+        "fused_ms": round(wall_ms, 4), "kernel_ms": round(mean_ms, 4), "kernel_median_ms": round(med_ms, 4),
+        "tflops": round(flops / (wall_ms * 1e-3) / 1e12, 2),
+        "kernel_tflops": round(flops / (mean_ms * 1e-3) / 1e12, 2),
+        "gemm_window_ms": round(gwin, 4) if gwin else None,
+        "comm_window_ms": round(cwin, 4) if cwin else None,
+        "comm_bytes": w.comm_bytes,
+        "comm_gbps": round(w.comm_bytes / (cwin * 1e-3) / 1e9, 1) if cwin else None,
+        "sequential_ms": round(seq_wall, 4),
+        "seq_gemm_only_ms": round(sgwin, 4) if sgwin else None,
+        "seq_gemm_only_tflops": round(flops / (sgwin * 1e-3) / 1e12, 2) if sgwin else None,
+        "seq_comm_only_ms": round(scwin, 4) if scwin else None,
+        "seq_comm_only_gbps": round(w.comm_bytes / (scwin * 1e-3) / 1e9, 1) if scwin else None,
+        "fused_le_sequential": wall_ms <= seq_wall,
+    }
+    res["mfma_frac"] = round(res["kernel_tflops"] / PEAK_FP16_TFLOPS, 4)
+    if res["comm_gbps"]:
+        res["comm_hbm_frac"] = round(res["comm_gbps"] / PEAK_HBM_GBPS, 4)
+    if res["seq_comm_only_gbps"]:
+        res["seq_comm_only_hbm_frac"] = round(res["seq_comm_only_gbps"] / PEAK_HBM_GBPS, 4)
+    return res, case
+
+
+def cpu_baseline(case):
+    """The oracle on the full headline problem; returns the report and the
+    number of output elements outside tolerance when compared to the GPU."""
+    import numpy as np
+    import oracle
+    w = case.w
+    threads = min(16, len(os.sched_getaffinity(0)))
+    shards = [s.cpu().numpy() for s in case.inp["shards"]]
+    B = case.inp["B"].cpu().numpy()
+    bias = case.inp["bias"].cpu().numpy()
+    log(f"[cpu_baseline] oracle all_gather_matmul {w.M}x{w.N}x{w.K} on {threads} threads")
+    t0 = time.perf_counter()
+    ref = oracle.all_gather_matmul(shards, B, bias, nthreads=threads)
+    dt = time.perf_counter() - t0
+    got = case.C.float().cpu().numpy().astype(np.float64)
+    bad = int((~(np.abs(got - ref) <= 1e-2 + 1e-2 * np.abs(ref))).sum())
+    gathered_ok = bool(np.array_equal(oracle.all_gather_k(shards), case.G.cpu().numpy().view(np.uint16)))
+    return {
+        "value": round(w.gemm_flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"full {w.name} all_gather_matmul (gather + {w.M}x{w.N}x{w.K} GEMM + bias, fp64), "
+                  f"{dt:.1f} s",
+        "seconds": round(dt, 2),
+    }, bad, gathered_ok
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 29  # 1 GiB of fp16
+    src = torch.ones(n, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "launches": 3}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the fused ops on a single MI355X; "
+              f"--gpus {args.gpus} is not supported (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    head, case = measure(args.workload, args.steps, args.warmup, not args.no_sweep)
+    cpu = None
+    if not args.no_cpu_baseline and case.w.op == "ag_mm" and case.w.gemm_flops <= 2 ** 38:
+        cpu, bad, gathered_ok = cpu_baseline(case)
+        head["oracle_check"] = {"C_outside_tol": bad, "gathered_bit_exact": gathered_ok}
+        if bad or not gathered_ok:
+            log(f"ERROR: GPU output disagrees with the oracle ({bad} elements, gathered {gathered_ok})")
+    del case
+    torch.cuda.empty_cache()
+    extra = []
+    if not args.headline_only:
+        for name in ("llama7b_gate", "concurrent", "g2"):
+            if name == args.workload:
+                continue
+            steps = 5 if name == "g2" else max(5, args.steps // 2)
+            r, c = measure(name, steps, 2, not args.no_sweep)
+            extra.append(r)
+            del c
+            torch.cuda.empty_cache()
+    w = head
+    line = {
+        "metric": "GEMM TFLOP/s + comm-tile GB/s on 1 MI355X, as fraction of MFMA/HBM peak",
+        "value": w["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": w["fused_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w['workload']} {'all_gather_matmul' if w['op'] == 'ag_mm' else w['op']} local share "
+                        f"(W={w['W']}, M={w['M']}, N={w['N']}, K={w['K']})",
+            "mode": "fused", "tile": w["tile"], "gemm_wgs": w["gemm_wgs"], "grid": w["grid"],
+            "accumulate": "f32",
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": w["kernel_tflops"], "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+            "frac": w["mfma_frac"], "traffic": None,
+            "kernel": f"persistent_kernel (fused {w['op']}), mean of {args.steps} launches: {w['kernel_ms']} ms",
+        },
+        "comm": {
+            "gbps": w["comm_gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": w.get("comm_hbm_frac"),
+            "window_ms": w["comm_window_ms"], "bytes": w["comm_bytes"],
+            "comm_only_gbps": w["seq_comm_only_gbps"], "comm_only_frac": w.get("seq_comm_only_hbm_frac"),
+        },
+        "sequential_ms": w["sequential_ms"],
+        "fused_le_sequential": w["fused_le_sequential"],
+        "cpu_baseline": cpu,
+        "detail": head,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -223,8 +223,8 @@ int resolve_device(Resolved* r, int kind, const DevInfo& di, const std::string& 
 }
 
 // ------------------------------------------------------------- workspace
-constexpr int kMaxGrid = 2048;
-constexpr size_t kStampBytes = (size_t)kMaxGrid * 4 * sizeof(uint64_t);
+constexpr int kMaxGrid = iris::kMaxGrid;
+constexpr size_t kStampBytes = (size_t)kMaxGrid * 6 * sizeof(uint64_t);
 
 int64_t flag_words(int kind, int64_t M, int64_t N, int W, int bm, int bn) {
   const int64_t n_pm = (M + bm - 1) / bm, n_pn = (N + bn - 1) / bn;
@@ -246,6 +246,7 @@ std::map<std::pair<int, void*>, OwnedWs> g_ws;   // (device, stream) -> workspac
 struct LastLaunch {
   int dev;
   int grid;          // workgroups of the persistent launch
+  int comm_grid;     // workgroups of the sequential comm kernel (0 if fused)
   bool fused;
   size_t stamp_off;  // byte offset of the stamps in the workspace
 };
@@ -276,6 +277,9 @@ int get_workspace(int dev, void* stream, size_t need, void* user, size_t user_by
       w.ptr = nullptr;
       return fail(IRIS_ERR_NO_MEMORY, "hipMalloc of a %zu-byte workspace failed: %s", bytes, hipGetErrorString(e));
     }
+    // a fresh workspace starts zeroed; every op leaves it zeroed again
+    e = hipMemsetAsync(w.ptr, 0, bytes, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "workspace clear");
     w.bytes = bytes;
   }
   *out = w.ptr;
@@ -401,12 +405,14 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
   }
   p.ws = (int32_t*)ws;
   p.stamps = (uint64_t*)((char*)ws + ibytes);
+  p.comm_stamps = p.stamps + (size_t)kMaxGrid * 4;
   p.spin_limit = 1u << 24;
+  p.n_reset = (int)(ibytes / 4);
   p.steal = (r.flags & IRIS_FLAG_NO_STEAL) ? 0 : 1;
   const hipStream_t s = (hipStream_t)stream;
 
-  hipError_t e = iris::launch_reset(p.ws, (int)(ibytes / 4), s);
-  if (e != hipSuccess) return hip_fail(e, "reset launch");
+  hipError_t e = hipSuccess;
+  int comm_grid = 0;
   if (r.mode == IRIS_MODE_FUSED) {
     p.op = d.kind;
     p.fused = 1;
@@ -424,7 +430,7 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
     Params pc = p;
     pc.op = d.kind;
     pc.fused = 0;
-    const int comm_grid = di.cus * 4;
+    comm_grid = std::min(di.cus * 4, kMaxGrid);
     if (d.kind == iris::OP_AG) {
       e = iris::launch_comm_only(pc, comm_grid, s);
       if (e == hipSuccess) e = iris::launch_persistent(pg, r.bm, r.bn, r.grid, s);
@@ -436,7 +442,7 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
   }
   {
     std::lock_guard<std::mutex> lk(g_mu);
-    g_last[ws] = LastLaunch{dev, r.grid, r.mode == IRIS_MODE_FUSED, ibytes};
+    g_last[ws] = LastLaunch{dev, r.grid, comm_grid, r.mode == IRIS_MODE_FUSED, ibytes};
   }
   if (getenv("IRIS_LOCAL_DEBUG")) {
     e = hipStreamSynchronize(s);
@@ -444,7 +450,10 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
     int32_t err = 0;
     e = hipMemcpy(&err, p.ws + iris::kErr, 4, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "debug readback");
-    if (err) return fail(IRIS_ERR_DEVICE_TIMEOUT, "a device-side wait hit its poll bound");
+    if (err) {
+      (void)hipMemset(p.ws + iris::kErr, 0, 4);
+      return fail(IRIS_ERR_DEVICE_TIMEOUT, "a device-side wait hit its poll bound");
+    }
   }
   return IRIS_OK;
 }
@@ -707,10 +716,9 @@ int iris_last_windows(void* workspace, void* stream, double* gs_ns, double* ge_n
     if (lt == g_last.end()) return fail(IRIS_ERR_INVALID_ARG, "no launch recorded for this workspace");
     last = lt->second;
   }
-  if (!last.fused) return fail(IRIS_ERR_INVALID_ARG, "the last launch on this workspace was not fused");
   e = hipStreamSynchronize((hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-  std::vector<uint64_t> st((size_t)last.grid * 4);
+  std::vector<uint64_t> st((size_t)kMaxGrid * 6);
   e = hipMemcpy(st.data(), (char*)ws + last.stamp_off, st.size() * 8, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "stamp readback");
   DevInfo di;
@@ -721,7 +729,11 @@ int iris_last_windows(void* workspace, void* stream, double* gs_ns, double* ge_n
   for (int b = 0; b < last.grid; ++b) {
     const uint64_t* w = &st[(size_t)b * 4];
     if (w[1]) { gs = std::min(gs, w[0]); ge = std::max(ge, w[1]); }
-    if (w[3]) { cs = std::min(cs, w[2]); ce = std::max(ce, w[3]); }
+    if (last.fused && w[3]) { cs = std::min(cs, w[2]); ce = std::max(ce, w[3]); }
+  }
+  for (int b = 0; b < last.comm_grid; ++b) {  // sequential mode: the comm kernel's own stamps
+    const uint64_t* w = &st[(size_t)kMaxGrid * 4 + (size_t)b * 2];
+    if (w[1]) { cs = std::min(cs, w[0]); ce = std::max(ce, w[1]); }
   }
   lo = std::min(gs, cs);
   const double ns_per_tick = 1e6 / (double)di.wall_khz;

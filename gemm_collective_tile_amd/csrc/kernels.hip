@@ -211,24 +211,37 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(Params p) {
       }
     }
   }
-  if (threadIdx.x == 0 && p.stamps) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
     uint64_t* st = p.stamps + (size_t)blockIdx.x * 4;
     st[0] = gs;
     st[1] = ge;
     st[2] = cs;
     st[3] = ce;
+    // everything this workgroup did to the counters and flags precedes this
+    const int done = __hip_atomic_fetch_add(p.ws + kDone, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    slot[0] = (done == (int)gridDim.x - 1);
+  }
+  __syncthreads();
+  if (slot[0]) {  // last workgroup out: leave the workspace zeroed for the next op
+    for (int i = threadIdx.x; i < p.n_reset; i += kThreads)
+      if (i != kErr) p.ws[i] = 0;
   }
 }
 
 // Sequential-mode comm kernel: every unit, no flags, grid-strided.
 template <int OP>
 __global__ __launch_bounds__(kThreads) void comm_only_kernel(Params p) {
-  for (int u = blockIdx.x; u < p.T_comm; u += gridDim.x) run_comm_unit<OP>(p, u);
-}
-
-__global__ __launch_bounds__(kThreads) void reset_kernel(int32_t* ws, int n) {
-  const int i = blockIdx.x * kThreads + threadIdx.x;
-  if (i < n) ws[i] = 0;
+  uint64_t cs = ~0ull, ce = 0;
+  for (int u = blockIdx.x; u < p.T_comm; u += gridDim.x) {
+    if (cs == ~0ull) cs = stamp_now();
+    run_comm_unit<OP>(p, u);
+    ce = stamp_now();
+  }
+  if (threadIdx.x == 0) {
+    p.comm_stamps[(size_t)blockIdx.x * 2] = cs;
+    p.comm_stamps[(size_t)blockIdx.x * 2 + 1] = ce;
+  }
 }
 
 // --------------------------------------------------------------- launchers
@@ -280,12 +293,6 @@ hipError_t launch_comm_only(const Params& p, int grid, hipStream_t s) {
     default:
       return hipErrorInvalidValue;
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_reset(int32_t* ws, int n_words, hipStream_t s) {
-  const int grid = (n_words + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL(reset_kernel, dim3(grid), dim3(kThreads), 0, s, ws, n_words);
   return hipGetLastError();
 }
 

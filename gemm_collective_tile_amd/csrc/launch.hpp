@@ -19,11 +19,17 @@ enum OpKind : int32_t {
 };
 
 // Workspace layout (int32 words):
-//   [0] GEMM queue counter   [1] comm queue counter   [2] error word
-//   [3] reserved             [kFlagBase ...] ready flags
-// followed (64-byte aligned) by uint64 stamps[G][4].
-constexpr int kCtrGemm = 0, kCtrComm = 1, kErr = 2;
+//   [0] GEMM queue counter   [1] comm queue counter   [2] error word (sticky)
+//   [3] finished-workgroup counter                    [kFlagBase ...] ready flags
+// followed (256-byte aligned) by uint64 stamps[kMaxGrid][4] written by the
+// persistent kernel and uint64 comm_stamps[kMaxGrid][2] written by the
+// sequential-mode comm kernel.
+// Every word but the error word is zero when a persistent launch starts; the
+// last workgroup to finish zeroes them again, so consecutive ops on one
+// workspace need no separate reset.
+constexpr int kCtrGemm = 0, kCtrComm = 1, kErr = 2, kDone = 3;
 constexpr int kFlagBase = 16;
+constexpr int kMaxGrid = 2048;
 
 struct Params {
   GemmArgs g;
@@ -37,12 +43,13 @@ struct Params {
   int32_t fused;             // 1: flags are produced and awaited in this launch
   int32_t* ws;               // counters + flags
   uint64_t* stamps;          // [gridDim.x][4]: gemm start/end, comm start/end
+  uint64_t* comm_stamps;     // [gridDim.x][2]: comm-only kernel start/end
   uint32_t spin_limit;       // bound on polls of one flag wait
+  int32_t n_reset;           // words [0, n_reset) (except kErr) to zero at the end
 };
 
 hipError_t launch_persistent(const Params& p, int bm, int bn, int grid, hipStream_t s);
 hipError_t launch_comm_only(const Params& p, int grid, hipStream_t s);
-hipError_t launch_reset(int32_t* ws, int n_words, hipStream_t s);
 // workgroups of the persistent kernel resident per CU, or <= 0 on error
 int persistent_blocks_per_cu(int bm, int bn, int op);
 bool tile_supported(int bm, int bn);

@@ -181,7 +181,10 @@ int iris_concurrent(void* C, const void* A, const void* B, const void* bias,
 
 /* Bytes of device workspace an op needs (0 on invalid arguments). The
  * workspace holds the two queue counters, the ready flags and per-workgroup
- * timestamps; callers passing their own must give at least this much. */
+ * timestamps. A caller passing its own must give at least this much, 256-byte
+ * aligned and ZERO-FILLED before its first use; every op leaves it zeroed
+ * again (the last workgroup of the launch clears what the launch used), so
+ * one zero fill serves any number of later ops. */
 size_t iris_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32_t W,
                            const iris_config_t* cfg);
 
@@ -220,10 +223,13 @@ int iris_tune_gemm_wgs(const iris_op_args_t* args, const int32_t* candidates,
                        float* ms_out, void* stream);
 
 /*
- * Per-workgroup timestamps of the last fused launch that used `workspace`
- * (or the library's own workspace for `stream` if workspace is NULL), in
- * nanoseconds since the earliest stamp: the windows in which GEMM tiles and
- * comm units ran. Waits for `stream`. Any output may be NULL.
+ * Windows of the last op that used `workspace` (or the library's own
+ * workspace for `stream` if workspace is NULL), from per-workgroup device
+ * timestamps, in nanoseconds since the earliest stamp: the first start and
+ * last end of any GEMM tile, and of any comm unit. In sequential mode the
+ * comm window comes from the comm kernel and the GEMM window from the GEMM
+ * kernel. A window with no work reads -1. Waits for `stream`. Any output may
+ * be NULL.
  */
 int iris_last_windows(void* workspace, void* stream, double* gemm_start_ns,
                       double* gemm_end_ns, double* comm_start_ns,
