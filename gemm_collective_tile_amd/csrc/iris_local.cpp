@@ -248,7 +248,7 @@ struct LastLaunch {
   int grid;          // workgroups of the persistent launch
   int comm_grid;     // workgroups of the sequential comm kernel (0 if fused)
   bool fused;
-  size_t stamp_off;  // byte offset of the stamps in the workspace
+  size_t stamp_off;  // byte offset of the stamps in the workspace (0)
 };
 std::map<void*, LastLaunch> g_last;  // workspace -> its last launch
 
@@ -403,8 +403,11 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
       p.T_comm = (int)((d.comm_elems + r.comm_chunk - 1) / r.comm_chunk);
       break;
   }
-  p.ws = (int32_t*)ws;
-  p.stamps = (uint64_t*)((char*)ws + ibytes);
+  // Layout: the timestamp block at a fixed offset 0, then the counters and
+  // flags. The flag region's size depends on the op; with the stamps first,
+  // no op's stamps can land on another op's flag words.
+  p.stamps = (uint64_t*)ws;
+  p.ws = (int32_t*)((char*)ws + kStampBytes);
   p.comm_stamps = p.stamps + (size_t)kMaxGrid * 4;
   p.spin_limit = 1u << 24;
   p.n_reset = (int)(ibytes / 4);
@@ -442,7 +445,7 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
   }
   {
     std::lock_guard<std::mutex> lk(g_mu);
-    g_last[ws] = LastLaunch{dev, r.grid, comm_grid, r.mode == IRIS_MODE_FUSED, ibytes};
+    g_last[ws] = LastLaunch{dev, r.grid, comm_grid, r.mode == IRIS_MODE_FUSED, 0};
   }
   if (getenv("IRIS_LOCAL_DEBUG")) {
     e = hipStreamSynchronize(s);

@@ -65,9 +65,20 @@ __device__ __forceinline__ int claim(int* ctr, int T, int* slot) {
   return v < T ? v : -1;
 }
 
+// Release of a unit's results to other workgroups (any XCD): every wave
+// drains its stores to L2, the workgroup barriers, then one thread writes the
+// XCD's L2 back (agent-scope release fence), waits for that write-back to
+// finish, and only then sets the flag. The explicit wait matters: once the
+// stores are drained the compiler sees nothing outstanding and would issue
+// the flag store right behind the write-back.
 __device__ __forceinline__ void publish(int* flag) {
-  __syncthreads();  // every thread's stores of the unit precede the release
-  if (threadIdx.x == 0) st_release(flag, 1);
+  drain_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    drain_vmem();
+    __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ------------------------------------------------------------ comm units

@@ -18,12 +18,11 @@ enum OpKind : int32_t {
   OP_CONC_AR = 4,     // comm: independent flat all_reduce units
 };
 
-// Workspace layout (int32 words):
+// Workspace layout: first uint64 stamps[kMaxGrid][4] written by the
+// persistent kernel and uint64 comm_stamps[kMaxGrid][2] written by the
+// sequential-mode comm kernel (a fixed-size block), then the int32 words
 //   [0] GEMM queue counter   [1] comm queue counter   [2] error word (sticky)
 //   [3] finished-workgroup counter                    [kFlagBase ...] ready flags
-// followed (256-byte aligned) by uint64 stamps[kMaxGrid][4] written by the
-// persistent kernel and uint64 comm_stamps[kMaxGrid][2] written by the
-// sequential-mode comm kernel.
 // Every word but the error word is zero when a persistent launch starts; the
 // last workgroup to finish zeroes them again, so consecutive ops on one
 // workspace need no separate reset.

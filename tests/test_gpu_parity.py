@@ -273,3 +273,25 @@ def test_repeat_runs_bit_identical():
         C, Gb = run_ag(inp)
         assert_bits_equal(C, C0, f"repeat {i}")
         assert_bits_equal(Gb, G0, f"repeat {i} gathered")
+
+
+def test_workspace_shared_across_layouts():
+    """Ops with different tile shapes share the library's per-stream
+    workspace; flags of one layout must never alias another op's bookkeeping
+    (regression: per-workgroup timestamps once sat right after the flag
+    region and a large-tile op's stamps read as "tile ready" flags of a
+    later small-tile op)."""
+    W, M, N, K = 4, 300, 800, 136
+    inp = rs_inputs(M, N, K, W, seed=5)
+    ref = oracle.matmul_reduce_scatter(host(inp["A"]), host(inp["B"]), [host(p) for p in inp["partials"]],
+                                       W, rank=0, bias=host(inp["bias"]))
+    for fill in (float("nan"), 0.0):
+        for tile in [(256, 256), (128, 128), (64, 64), (256, 128), (64, 64)]:
+            note(f"shared workspace: tile={tile} fill={fill}")
+            A, B, bias, parts = cuda(inp["A"]), cuda(inp["B"]), cuda(inp["bias"]), cuda(inp["partials"])
+            C = torch.full((M, N), fill, dtype=torch.float16, device="cuda")
+            out = torch.full((M, N // W), fill, dtype=torch.float16, device="cuda")
+            il.iris_mm_rs_local(out, C, A, B, parts, W, rank=0, bias=bias,
+                                config=Config(block_m=tile[0], block_n=tile[1], comm_block_n=64))
+            torch.cuda.synchronize()
+            assert_close(out, ref, f"out tile={tile} fill={fill}")
