@@ -1,0 +1,129 @@
+"""Parity at the full workload sizes, in the launch configurations bench.py
+times (default 256x256 tiles; the gemm_wgs candidates of its sweep).
+
+Large GEMM outputs are checked on 64 sampled 128x128 tiles (always including
+the first and the last) computed one by one by the oracle; the copy and
+reduce outputs are checked over the whole buffer: the gathered buffer bit for
+bit, the reduce_scatter slice and the all_reduce output within tolerance.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_util import assert_bits_equal, assert_close, host, note
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import gemm_collective_tile_amd as il
+    from gemm_collective_tile_amd import Config
+else:
+    il = None
+    Config = None
+
+TILE = 128
+NTILES = 64
+
+
+def sweep_candidates():
+    G = il.iris_grid_size(None)
+    return sorted({max(1, min(G - 1, int(math.floor(f * G)))) for f in (0.5, 0.75, 0.875)})
+
+
+def check_sampled_tiles(C: torch.Tensor, ref_fn, what: str) -> None:
+    M, N = C.shape
+    tiles = wl.sample_tiles(M, N, TILE, NTILES, seed=0)
+    for (r0, c0) in tiles:
+        r1, c1 = min(M, r0 + TILE), min(N, c0 + TILE)
+        assert_close(C[r0:r1, c0:c1], ref_fn(r0, r1, c0, c1), f"{what} tile ({r0},{c0})")
+
+
+def ag_tile_ref(inp):
+    B_host = {}
+
+    def ref(r0, r1, c0, c1):
+        shards = [host(s[r0:r1]) for s in inp["shards"]]
+        if c0 not in B_host:
+            B_host[c0] = host(inp["B"][:, c0:c1].contiguous())
+        bias = host(inp["bias"][c0:c1])
+        return oracle.all_gather_matmul(shards, B_host[c0], bias)
+    return ref
+
+
+def check_gathered(G: torch.Tensor, shards, chunk_rows=8192):
+    M = G.shape[0]
+    for r0 in range(0, M, chunk_rows):
+        r1 = min(M, r0 + chunk_rows)
+        ref = oracle.all_gather_k([host(s[r0:r1]) for s in shards])
+        assert_bits_equal(G[r0:r1], ref.view(np.float16), f"gathered rows {r0}:{r1}")
+
+
+def test_pow2_4k_all_gather_matmul():
+    w = wl.WORKLOADS["pow2_4k"]
+    inp = wl.make_inputs(w, seed=0, device="cuda")
+    ref = ag_tile_ref(inp)
+    first = None
+    for gw in sweep_candidates():
+        note(f"pow2_4k fused gemm_wgs={gw}")
+        C = torch.full((w.M, w.N), float("nan"), dtype=torch.float16, device="cuda")
+        G = torch.full((w.M, w.K), float("nan"), dtype=torch.float16, device="cuda")
+        il.iris_ag_mm(C, G, inp["shards"], inp["B"], inp["bias"], config=Config(gemm_wgs=gw))
+        torch.cuda.synchronize()
+        check_gathered(G, inp["shards"])
+        if first is None:
+            check_sampled_tiles(C, ref, "pow2_4k C")
+            first = C
+        else:
+            assert_bits_equal(C, first, f"schedule invariance gemm_wgs={gw}")
+
+
+def test_llama7b_gate_reduce_scatter():
+    w = wl.WORKLOADS["llama7b_gate"]
+    inp = wl.make_inputs(w, seed=0, device="cuda")
+    note("llama7b_gate fused reduce_scatter")
+    C = torch.full((w.M, w.N), float("nan"), dtype=torch.float16, device="cuda")
+    out = torch.full((w.M, w.N_local), float("nan"), dtype=torch.float16, device="cuda")
+    il.iris_mm_rs_local(out, C, inp["A"], inp["B"], inp["partials"], w.W, rank=w.rank, bias=inp["bias"])
+    torch.cuda.synchronize()
+    A, B, bias = host(inp["A"]), host(inp["B"]), host(inp["bias"])
+    note("llama7b_gate oracle: full reduce_scatter slice")
+    ref = oracle.matmul_reduce_scatter(A, B, [host(p) for p in inp["partials"]], w.W, rank=w.rank,
+                                       bias=bias)
+    assert_close(out, ref, "reduce_scatter out (full)")
+    check_sampled_tiles(C, lambda r0, r1, c0, c1: oracle.gemm_bias(A, B, bias, rows=(r0, r1), cols=(c0, c1)),
+                        "llama7b_gate C")
+
+
+def test_concurrent_gemm_and_all_reduce():
+    w = wl.WORKLOADS["concurrent"]
+    inp = wl.make_inputs(w, seed=0, device="cuda")
+    note("concurrent fused: GEMM 8192^3 beside all_reduce 8 x 64Mi")
+    C = torch.full((w.M, w.N), float("nan"), dtype=torch.float16, device="cuda")
+    out = torch.full((w.comm_elems,), float("nan"), dtype=torch.float16, device="cuda")
+    il.iris_concurrent(C, inp["A"], inp["B"], out, inp["comm_in"], bias=inp["bias"])
+    torch.cuda.synchronize()
+    note("concurrent oracle: full all_reduce")
+    aref = oracle.all_reduce([host(x) for x in inp["comm_in"]])
+    assert_close(out, aref, "all_reduce (full)")
+    B_host = host(inp["B"])
+    bias = host(inp["bias"])
+    check_sampled_tiles(C, lambda r0, r1, c0, c1: oracle.gemm_bias(host(inp["A"][r0:r1]), B_host, bias,
+                                                                   cols=(c0, c1)), "concurrent C")
+
+
+def test_g2_all_gather_matmul():
+    w = wl.WORKLOADS["g2"]
+    inp = wl.make_inputs(w, seed=0, device="cuda")
+    note("g2 fused all_gather_matmul 131072x16384x16384")
+    C = torch.full((w.M, w.N), float("nan"), dtype=torch.float16, device="cuda")
+    G = torch.full((w.M, w.K), float("nan"), dtype=torch.float16, device="cuda")
+    il.iris_ag_mm(C, G, inp["shards"], inp["B"], inp["bias"])
+    torch.cuda.synchronize()
+    note("g2: full gathered buffer")
+    check_gathered(G, inp["shards"])
+    note("g2: 64 sampled tiles of C")
+    check_sampled_tiles(C, ag_tile_ref(inp), "g2 C")
