@@ -63,6 +63,7 @@ struct TileShape {
   static constexpr int A_STAGE = BM * RA;
   static constexpr int B_STAGE = BK * RB;
   static constexpr int STAGE = A_STAGE + B_STAGE;
+  static constexpr int B_RING = NSTAGE * A_STAGE;     // LDS: [A stages | B stages]
   static constexpr int LDS_BYTES = NSTAGE * STAGE;
   static constexpr int A_DMA = A_STAGE / 1024 / 4;    // 1 KiB DMA instructions per wave per step
   static constexpr int B_DMA = B_STAGE / 1024 / 4;
@@ -72,11 +73,23 @@ struct TileShape {
 };
 
 // swizzle of the 16-byte chunks of a 64-byte A row (4 chunks)
-__device__ __forceinline__ uint32_t swz_a(uint32_t r) { return ((r >> 1) ^ (r >> 3)) & 3u; }
+#ifndef IRIS_SWZ_A
+#define IRIS_SWZ_A 1
+#endif
+__device__ __forceinline__ uint32_t swz_a(uint32_t r) {
+  if (IRIS_SWZ_A == 1) return (r >> 2) & 3u;
+  if (IRIS_SWZ_A == 2) return r & 3u;
+  if (IRIS_SWZ_A == 3) return 0u;
+  if (IRIS_SWZ_A == 4) return ((r >> 1) ^ (r >> 2)) & 3u;
+  return ((r >> 1) ^ (r >> 3)) & 3u;
+}
 // swizzle of the 16-byte chunks of a B row, by k row
+#ifndef IRIS_SWZ_B_MUL
+#define IRIS_SWZ_B_MUL 4
+#endif
 template <class S>
 __device__ __forceinline__ uint32_t swz_b(uint32_t k) {
-  return ((k & 3u) << 2) & (uint32_t)(S::CPR_B - 1);
+  return ((k & 3u) * IRIS_SWZ_B_MUL) & (uint32_t)(S::CPR_B - 1);
 }
 
 struct GemmArgs {
@@ -93,29 +106,34 @@ struct GemmArgs {
 
 template <class S>
 struct GemmPipe {
-  // per-thread global offsets of the DMA chunks of the current tile
+  // per-lane byte offsets of the DMA chunks within a K step's resource
   uint32_t a_off[S::A_DMA];
-  uint32_t a_kc[S::A_DMA];  // k offset (elements) of that chunk within a step
+  uint32_t a_kc;             // k offset (elements) of this lane's A chunks
   uint32_t b_off[S::B_DMA];
-  // LDS byte offsets within a stage of the fragment reads
+  // LDS byte offsets of the fragment reads within the A / B rings
   uint32_t ra_base[2];        // A, per k slice
-  uint32_t rb_base[S::FN];    // B, per 32-column block
+  uint32_t rb_base[S::FN];    // B, per 32-column block (includes B_RING)
+  uint32_t wave;              // wave index, uniform (scalar)
 
   __device__ __forceinline__ void setup(const GemmArgs& g, int n0) {
-    const uint32_t l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint32_t l = threadIdx.x & 63;
+    const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t wm = w >> 1, wn = w & 1;
+    wave = w;
+    // A instruction b covers tile rows 16 b .. 16 b + 15: lane l takes row
+    // 16 b + (l >> 2) and LDS chunk l & 3, i.e. logical chunk (l & 3) ^ swz
+    // (swz_a(16 b + r) == swz_a(r), so the chunk is the same for every b)
+    const uint32_t ca = (l & 3) ^ swz_a(l >> 2);
+    a_kc = 8 * ca;
 #pragma unroll
     for (int n = 0; n < S::A_DMA; ++n) {
-      const uint32_t b = w * S::A_DMA + n;
-      const uint32_t r = 16 * b + (l >> 2);
-      const uint32_t c = (l & 3) ^ swz_a(r);
-      a_off[n] = (uint32_t)((r * g.lda + 8 * c) * 2);
-      a_kc[n] = 8 * c;
+      const uint32_t r = 16 * (w * S::A_DMA + n) + (l >> 2);
+      a_off[n] = (uint32_t)((r * g.lda + 8 * ca) * 2);
     }
 #pragma unroll
     for (int n = 0; n < S::B_DMA; ++n) {
-      const uint32_t b = w * S::B_DMA + n;
-      const uint32_t k = S::RPB * b + l / S::CPR_B;
+      // B instruction b covers k rows RPB b .. RPB b + RPB - 1
+      const uint32_t k = S::RPB * (w * S::B_DMA + n) + l / S::CPR_B;
       const uint32_t c = (l % S::CPR_B) ^ swz_b<S>(k);
       const bool ok = n0 + 8 * (int)c < g.N;
       b_off[n] = ok ? (uint32_t)((k * g.ldb + 8 * c) * 2) : kOob;
@@ -124,7 +142,7 @@ struct GemmPipe {
       const uint32_t r = wm * S::WTM + (l & 31);
       const uint32_t h = l >> 5;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) ra_base[s] = r * S::RA + (((2 * s + h) ^ swz_a(r)) << 4);
+      for (int sl = 0; sl < 2; ++sl) ra_base[sl] = r * S::RA + (((2 * sl + h) ^ swz_a(r)) << 4);
     }
     {
       const uint32_t grp = l >> 4, e = (l >> 2) & 3, q = l & 3;
@@ -132,30 +150,39 @@ struct GemmPipe {
 #pragma unroll
       for (int j = 0; j < S::FN; ++j) {
         const uint32_t c = (wn * S::WTN + 32 * j) / 8 + 2 * (grp & 1) + (q >> 1);
-        rb_base[j] = S::A_STAGE + k * S::RB + ((c ^ swz_b<S>(k)) << 4) + 8 * (q & 1);
+        rb_base[j] = S::B_RING + k * S::RB + ((c ^ swz_b<S>(k)) << 4) + 8 * (q & 1);
       }
     }
   }
 
-  // issue the LDS DMA of K step `step` (k0 = step * BK) into `stage`
-  __device__ __forceinline__ void issue(const GemmArgs& g, int m0, int n0, int step, uint32_t lds_base,
-                                        uint32_t stage) const {
-    const uint32_t w = threadIdx.x >> 6;
+  // Buffer resources of K step `step` (k0 = step * BK): rows past M and K
+  // fall outside them.
+  struct Rsrc {
+    u32x4 a, b;
+    bool kok;
+  };
+  __device__ __forceinline__ Rsrc rsrc(const GemmArgs& g, int m0, int n0, int step) const {
+    Rsrc r;
     const int k0 = step * S::BK;
     const int rows = min(S::BM, g.M - m0);
     const int64_t abytes = (int64_t)rows * g.lda * 2 - (int64_t)k0 * 2;
-    const u32x4 ra = rsrc_words(g.A + (int64_t)m0 * g.lda + k0, abytes > 0 ? (uint32_t)abytes : 0u);
+    r.a = rsrc_words(g.A + (int64_t)m0 * g.lda + k0, abytes > 0 ? (uint32_t)abytes : 0u);
     const int krows = min(S::BK, g.K - k0);
-    const u32x4 rb = rsrc_words(g.B + (int64_t)k0 * g.ldb + n0,
-                                krows > 0 ? (uint32_t)((int64_t)krows * g.ldb * 2 - (int64_t)n0 * 2) : 0u);
-#pragma unroll
-    for (int n = 0; n < S::A_DMA; ++n) {
-      const uint32_t off = (k0 + (int)a_kc[n] < g.K) ? a_off[n] : kOob;
-      dma16(ra, lds_base + stage + (w * S::A_DMA + n) * 1024, off);
+    r.b = rsrc_words(g.B + (int64_t)k0 * g.ldb + n0,
+                     krows > 0 ? (uint32_t)((int64_t)krows * g.ldb * 2 - (int64_t)n0 * 2) : 0u);
+    r.kok = k0 + (int)a_kc < g.K;
+    return r;
+  }
+
+  // DMA number D (A instructions first, then B) of a K step into ring slot ST
+  template <int D>
+  __device__ __forceinline__ void dma(const Rsrc& r, uint32_t lds_base, int ST) const {
+    if constexpr (D < S::A_DMA) {
+      dma16(r.a, lds_base + ST * S::A_STAGE + (wave * S::A_DMA + D) * 1024, r.kok ? a_off[D] : kOob);
+    } else {
+      constexpr int n = D - S::A_DMA;
+      dma16(r.b, lds_base + S::B_RING + ST * S::B_STAGE + (wave * S::B_DMA + n) * 1024, b_off[n]);
     }
-#pragma unroll
-    for (int n = 0; n < S::B_DMA; ++n)
-      dma16(rb, lds_base + stage + S::A_STAGE + (w * S::B_DMA + n) * 1024, b_off[n]);
   }
 
   struct Frags {
@@ -163,15 +190,18 @@ struct GemmPipe {
     f16x8 b[S::FN];
   };
 
-  // fragments of k slice SL (0 or 1) of the step held in `stage`
-  template <int SL>
-  __device__ __forceinline__ void read(const char* lds, uint32_t stage, Frags& f) const {
-#pragma unroll
-    for (int i = 0; i < S::FM; ++i)
-      f.a[i] = as_h8(*(const u32x4*)(lds + stage + ra_base[SL] + i * 32 * S::RA));
-#pragma unroll
-    for (int j = 0; j < S::FN; ++j) {
-      const char* p = lds + stage + rb_base[j] + SL * 16 * S::RB;
+  // fragment read item X of k slice SL from ring slot ST: items alternate
+  // a0, b0, a1, b1, ... so that the operands of the first MFMA blocks arrive
+  // first
+  template <int SL, int X>
+  __device__ __forceinline__ void read(const char* lds, int ST, Frags& f) const {
+    constexpr int NMIN = S::FM < S::FN ? S::FM : S::FN;
+    constexpr bool IS_A = X < 2 * NMIN ? (X % 2 == 0) : (S::FM > S::FN);
+    constexpr int IDX = X < 2 * NMIN ? X / 2 : X - NMIN;
+    if constexpr (IS_A) {
+      f.a[IDX] = as_h8(*(const u32x4*)(lds + ra_base[SL] + ST * S::A_STAGE + IDX * 32 * S::RA));
+    } else {
+      const char* p = lds + rb_base[IDX] + ST * S::B_STAGE + SL * 16 * S::RB;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 4 * S::RB));
       u32x4 v;
@@ -179,28 +209,145 @@ struct GemmPipe {
       v[1] = __builtin_bit_cast(u32x2, lo)[1];
       v[2] = __builtin_bit_cast(u32x2, hi)[0];
       v[3] = __builtin_bit_cast(u32x2, hi)[1];
-      f.b[j] = as_h8(v);
+      f.b[IDX] = as_h8(v);
     }
   }
 };
 
-template <class S>
-__device__ __forceinline__ void mma(f32x16 (&acc)[S::FM][S::FN], const typename GemmPipe<S>::Frags& f,
-                                    int j0, int j1) {
-#pragma unroll
-  for (int i = 0; i < S::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < S::FN; ++j)
-      if (j >= j0 && j < j1)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+// MFMA block K of a k slice: row block K / FN, column block K % FN
+template <class S, int K>
+__device__ __forceinline__ void mma_block(f32x16 (&acc)[S::FM][S::FN], const typename GemmPipe<S>::Frags& f) {
+  constexpr int i = K / S::FN, j = K % S::FN;
+  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
-// s_waitcnt with only the vector-memory counter limited to N (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+// s_waitcnt with the vector-memory counter limited to VM and the LDS counter
+// to LG (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+template <int VM, int LG = 15>
+__device__ __forceinline__ void wait_cnt() {
+  static_assert(VM >= 0 && VM < 64 && LG >= 0 && LG < 16, "counter range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LG << 8));
+}
+
+// Slots of a K step, issued in program order:
+//   region 1: slot k = MFMA block k of slice 0 (fragments f0), then fragment
+//             read item k of slice 1 into f1, then DMA k - (NM - ND) of step
+//             t+3; then the first half of slice 1's MFMA blocks.
+//   wait for this wave's DMAs of step t+1 and its own LDS reads; barrier.
+//   region 2: the second half of slice 1's blocks, each followed by two
+//             fragment reads of slice 0 of step t+1 (stage NXT) into f0.
+template <class S, int K, int NM, int NR, int ND>
+__device__ __forceinline__ void region1(const GemmPipe<S>& P, const typename GemmPipe<S>::Rsrc& r,
+                                        const char* lds, uint32_t lds_base, int cur, int ahead,
+                                        typename GemmPipe<S>::Frags& f0, typename GemmPipe<S>::Frags& f1,
+                                        f32x16 (&acc)[S::FM][S::FN]) {
+  constexpr int SLOTS = NM > NR ? (NM > ND ? NM : ND) : (NR > ND ? NR : ND);
+  if constexpr (K < SLOTS) {
+    if constexpr (K < NM) mma_block<S, K>(acc, f0);
+    if constexpr (K < NR) P.template read<1, K>(lds, cur, f1);
+    constexpr int D = K - (SLOTS - ND);
+    if constexpr (D >= 0 && D < ND) P.template dma<D>(r, lds_base, ahead);
+    region1<S, K + 1, NM, NR, ND>(P, r, lds, lds_base, cur, ahead, f0, f1, acc);
+  }
+}
+
+template <class S, int K, int K1, int NM>
+__device__ __forceinline__ void mma_range(f32x16 (&acc)[S::FM][S::FN], const typename GemmPipe<S>::Frags& f) {
+  if constexpr (K < K1 && K < NM) {
+    mma_block<S, K>(acc, f);
+    mma_range<S, K + 1, K1, NM>(acc, f);
+  }
+}
+
+template <class S, int K, int NM, int NR, int X>
+__device__ __forceinline__ void region2(const GemmPipe<S>& P, const char* lds, int nxt,
+                                        typename GemmPipe<S>::Frags& f0, const typename GemmPipe<S>::Frags& f1,
+                                        f32x16 (&acc)[S::FM][S::FN]) {
+  if constexpr (K < NM || X < NR) {
+    if constexpr (K < NM) mma_block<S, K>(acc, f1);
+    if constexpr (X < NR) P.template read<0, X>(lds, nxt, f0);
+    if constexpr (X + 1 < NR) P.template read<0, X + 1>(lds, nxt, f0);
+    region2<S, K + 1, NM, NR, X + 2>(P, lds, nxt, f0, f1, acc);
+  }
+}
+
+// Scheduling groups (masks of __builtin_amdgcn_sched_group_barrier: 0x8
+// MFMA, 0x100 LDS read). Region 1: slot k = one MFMA, then the LDS reads of
+// fragment item k (1 for an A item, 2 for a B item). Region 2: one MFMA, then
+// the reads of two items. The DMA (inline asm) keeps its program order.
+template <class S>
+__device__ constexpr int item_reads(int x) {
+  constexpr int NMIN = S::FM < S::FN ? S::FM : S::FN;
+  if (x >= S::FM + S::FN) return 0;
+  const bool is_a = x < 2 * NMIN ? (x % 2 == 0) : (S::FM > S::FN);
+  return is_a ? 1 : 2;
+}
+
+template <class S, int K, int NM>
+__device__ __forceinline__ void sched_region1() {
+  if constexpr (K < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (item_reads<S>(K) > 0) __builtin_amdgcn_sched_group_barrier(0x100, item_reads<S>(K), 0);
+    sched_region1<S, K + 1, NM>();
+  }
+}
+
+template <class S, int K, int NM, int X>
+__device__ __forceinline__ void sched_region2() {
+  if constexpr (K < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int R = item_reads<S>(X) + item_reads<S>(X + 1);
+    if constexpr (R > 0) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    sched_region2<S, K + 1, NM, X + 2>();
+  }
+}
+
+// One K step on ring slot ST (compile-time), fragments of slice 0 already
+// in f0. Loads step t+3 into slot (ST+3) % NSTAGE.
+template <class S, int ST>
+__device__ __forceinline__ void k_step(const GemmPipe<S>& P, const GemmArgs& g, int m0, int n0, int t,
+                                       const char* lds, uint32_t lds_base, typename GemmPipe<S>::Frags& f0,
+                                       typename GemmPipe<S>::Frags& f1, f32x16 (&acc)[S::FM][S::FN]) {
+  constexpr int NS = S::NSTAGE;
+  constexpr int CUR = ST % NS, NXT = (ST + 1) % NS, AHEAD = (ST + NS - 1) % NS;
+  constexpr int NM = S::FM * S::FN, NR = S::FM + S::FN, ND = S::A_DMA + S::B_DMA;
+  constexpr int H1 = NM / 2;
+  // keep the scheduler from hoisting this step's reads into the previous
+  // step (that would hold three fragment sets live and spill)
+  __builtin_amdgcn_sched_barrier(0);
+  const typename GemmPipe<S>::Rsrc r = P.rsrc(g, m0, n0, t + NS - 1);
+  region1<S, 0, NM, NR, ND>(P, r, lds, lds_base, CUR, AHEAD, f0, f1, acc);
+  mma_range<S, 0, H1, NM>(acc, f1);
+  sched_region1<S, 0, NM + H1>();
+  // step t+1 complete for this wave (t+2 and t+3 may be in flight), and
+  // every fragment read of this slot done, before the barrier. The barrier
+  // must carry the workgroup fences: without them the compiler may hoist the
+  // next step's LDS reads above it.
+  __builtin_amdgcn_sched_barrier(0);
+  wait_cnt<(NS - 2) * ND, 0>();
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+  region2<S, H1, NM, NR, 0>(P, lds, NXT, f0, f1, acc);
+  sched_region2<S, H1, NM, 0>();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <class S, int D, int ND>
+__device__ __forceinline__ void dma_all(const GemmPipe<S>& P, const typename GemmPipe<S>::Rsrc& r,
+                                        uint32_t lds_base, int slot) {
+  if constexpr (D < ND) {
+    P.template dma<D>(r, lds_base, slot);
+    dma_all<S, D + 1, ND>(P, r, lds_base, slot);
+  }
+}
+
+template <class S, int X, int NR>
+__device__ __forceinline__ void read_all(const GemmPipe<S>& P, const char* lds, int slot,
+                                         typename GemmPipe<S>::Frags& f) {
+  if constexpr (X < NR) {
+    P.template read<0, X>(lds, slot, f);
+    read_all<S, X + 1, NR>(P, lds, slot, f);
+  }
 }
 
 // Computes the tile at (m0, n0) and writes it to C. `lds` must hold
@@ -210,7 +357,8 @@ template <class S>
 __device__ void gemm_tile(const GemmArgs& g, int m0, int n0, char* lds) {
   using P_t = GemmPipe<S>;
   constexpr int NS = S::NSTAGE;
-  constexpr int PER_STEP = S::A_DMA + S::B_DMA;  // DMA instructions per wave per step
+  constexpr int ND = S::A_DMA + S::B_DMA;  // DMA instructions per wave per step
+  constexpr int NR = S::FM + S::FN;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -227,37 +375,33 @@ __device__ void gemm_tile(const GemmArgs& g, int m0, int n0, char* lds) {
   P_t P;
   P.setup(g, n0);
   typename P_t::Frags f0, f1;
-
   // LDS byte address of the stage ring, for the DMA
-  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t*)lds;
-  __syncthreads();  // previous users of the LDS are done
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s) P.issue(g, m0, n0, s, lds_base, s * S::STAGE);
-  wait_vmcnt<(NS - 2) * PER_STEP>();  // this wave's part of step 0 has landed
-  __syncthreads();
-  P.template read<0>(lds, 0, f0);
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)lds);
 
-  for (int t = 0; t < nk; ++t) {
-    const uint32_t cur = (uint32_t)(t % NS) * S::STAGE;
-    const uint32_t nxt = (uint32_t)((t + 1) % NS) * S::STAGE;
-    const uint32_t ahead = (uint32_t)((t + NS - 1) % NS) * S::STAGE;
-    // slice 0: MFMAs on f0 under the loads of step t+3 and the reads of slice 1
-    P.issue(g, m0, n0, t + NS - 1, lds_base, ahead);
-    P.template read<1>(lds, cur, f1);
-    mma<S>(acc, f0, 0, S::FN);
-    // slice 1, first half
-    mma<S>(acc, f1, 0, S::FN / 2);
-    // step t+1 must be complete for every wave before its fragments are read;
-    // the loads of steps t+2 and t+3 may still be in flight
-    wait_vmcnt<(NS - 2) * PER_STEP>();
-    __syncthreads();
-    P.template read<0>(lds, nxt, f0);
-    // slice 1, second half
-    mma<S>(acc, f1, S::FN / 2, S::FN);
+  __syncthreads();  // previous users of the LDS are done
+  dma_all<S, 0, ND>(P, P.rsrc(g, m0, n0, 0), lds_base, 0);
+  dma_all<S, 0, ND>(P, P.rsrc(g, m0, n0, 1), lds_base, 1);
+  dma_all<S, 0, ND>(P, P.rsrc(g, m0, n0, 2), lds_base, 2);
+  wait_cnt<(NS - 2) * ND>();  // this wave's part of step 0 has landed
+  __syncthreads();
+  read_all<S, 0, NR>(P, lds, 0, f0);
+
+  // The ring has NS = 4 slots: unroll by 4 so every slot offset is a
+  // constant. The step count is rounded up to a multiple of 4 (a loop with one
+  // exit keeps the accumulators in place); the extra steps read only
+  // out-of-range zeros and add exact zeros to accumulators that start at +0,
+  // so they change no bit of the result.
+  static_assert(NS == 4, "the K loop is unrolled by the ring size");
+  const int nk4 = (nk + 3) & ~3;
+  for (int t = 0; t < nk4; t += 4) {
+    k_step<S, 0>(P, g, m0, n0, t, lds, lds_base, f0, f1, acc);
+    k_step<S, 1>(P, g, m0, n0, t + 1, lds, lds_base, f0, f1, acc);
+    k_step<S, 2>(P, g, m0, n0, t + 2, lds, lds_base, f0, f1, acc);
+    k_step<S, 3>(P, g, m0, n0, t + 3, lds, lds_base, f0, f1, acc);
   }
   // loads issued past the last step target stages no one reads; let them
   // land before the LDS is reused
-  wait_vmcnt<0>();
+  wait_cnt<0, 0>();
 
   // epilogue: lane holds row m = lane & 31 of each 32x32 block and, for
   // q = 0..3, columns 8q + 4*(lane >> 5) + 0..3.
