@@ -231,8 +231,8 @@ __device__ __forceinline__ void wait_cnt() {
 
 // Slots of a K step, issued in program order:
 //   region 1: slot k = MFMA block k of slice 0 (fragments f0), then fragment
-//             read item k of slice 1 into f1, then DMA k - (NM - ND) of step
-//             t+3; then the first half of slice 1's MFMA blocks.
+//             read item k of slice 1 into f1, then DMA k of step t+3 (the
+//             DMAs go first so they have the most time to land); then the first half of slice 1's MFMA blocks.
 //   wait for this wave's DMAs of step t+1 and its own LDS reads; barrier.
 //   region 2: the second half of slice 1's blocks, each followed by two
 //             fragment reads of slice 0 of step t+1 (stage NXT) into f0.
@@ -245,7 +245,7 @@ __device__ __forceinline__ void region1(const GemmPipe<S>& P, const typename Gem
   if constexpr (K < SLOTS) {
     if constexpr (K < NM) mma_block<S, K>(acc, f0);
     if constexpr (K < NR) P.template read<1, K>(lds, cur, f1);
-    constexpr int D = K - (SLOTS - ND);
+    constexpr int D = K;
     if constexpr (D >= 0 && D < ND) P.template dma<D>(r, lds_base, ahead);
     region1<S, K + 1, NM, NR, ND>(P, r, lds, lds_base, cur, ahead, f0, f1, acc);
   }
