@@ -53,7 +53,7 @@ class IrisError(RuntimeError):
 
 class _Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "block_m", "block_n", "block_k", "group_m", "gemm_wgs", "comm_block_n", "comm_chunk",
+        "block_m", "block_n", "block_k", "group_m", "gemm_wgs", "comm_block_m", "comm_block_n", "comm_chunk",
         "mode", "flags")]
 
 
@@ -65,6 +65,7 @@ class Config:
     block_k: int = 0
     group_m: int = 0
     gemm_wgs: int = 0
+    comm_block_m: int = 0
     comm_block_n: int = 0
     comm_chunk: int = 0
     mode: int = IRIS_MODE_FUSED

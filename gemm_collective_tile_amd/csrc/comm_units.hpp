@@ -4,8 +4,8 @@
 //
 //   all_gather (Iris docs "Fused Communication and Compute Operations",
 //   all_gather_matmul): shard s of rank order lands in columns
-//   [s*K_local, (s+1)*K_local) of the gathered matrix. Unit (pm, s) copies
-//   rows [pm*BM, pm*BM+BM) of shard s. Bit copy.
+//   [s*K_local, (s+1)*K_local) of the gathered matrix. A unit copies
+//   `rows_u` rows of one shard (a slice of one GEMM row block). Bit copy.
 //
 //   reduce (same page, matmul_reduce_scatter and matmul_all_reduce; the
 //   all_reduce beside an independent GEMM of the iris.concurrent PR):
@@ -14,9 +14,15 @@
 //   rows x columns (reduce_scatter / matmul_all_reduce) or a flat chunk
 //   (concurrent all_reduce).
 //
-// Each thread moves 8 fp16 (16 bytes) per vector and keeps several vectors
-// in flight; a wavefront covers 1 KiB of contiguous row per load, and every
-// wavefront reduces its own vectors with no cross-lane traffic.
+// A CU moves only a few tens of GB/s, bounded by the memory requests its
+// waves keep in flight, so each thread issues all loads of a batch (up to 8
+// sources x U vectors of 16 bytes) before it consumes any of them; the adds
+// then run in source order. A wavefront covers 1 KiB of contiguous row per
+// load and reduces its own vectors with no cross-lane traffic. Data read
+// once by a reduce (partials, buffers) and its results, which nobody in the
+// kernel reads, use the streaming cache policy. The copy keeps the default
+// policy both ways: its shards are small enough to stay in the last-level
+// cache between calls, and the GEMM reads the gathered matrix next.
 #pragma once
 
 #include "device_common.hpp"
@@ -35,18 +41,21 @@ struct CommArgs {
   int32_t col0;           // rank * N_local (RS) or 0 (AR)
   int32_t ncols;          // N_local (RS) or N (AR): row length of src and dst
   int32_t comm_bn;        // columns per unit
-  int32_t n_cc;           // column chunks per row block
+  int32_t n_cc;           // column chunks per row slice
   // flat all_reduce
   int64_t elems;
   int32_t chunk;
   int32_t M, BM;
+  int32_t rows_u;         // rows per unit (divides BM)
+  int32_t n_sub;          // units per row block along M: BM / rows_u
 };
 
 // ------------------------------------------------------------- all_gather
+// Unit (pm, s, q): rows [pm*BM + q*rows_u, +rows_u) of shard s.
 template <int U>
-__device__ void ag_copy_unit(const CommArgs& a, int pm, int s) {
-  const int r0 = pm * a.BM;
-  const int rows = min(a.BM, a.M - r0);
+__device__ void ag_copy_unit(const CommArgs& a, int pm, int s, int q) {
+  const int r0 = pm * a.BM + q * a.rows_u;
+  const int rows = min(a.rows_u, a.M - r0);
   if (rows <= 0) return;
   const uint32_t vpr = (uint32_t)(a.K_local >> 3);  // 16-byte vectors per row
   const uint32_t total = (uint32_t)rows * vpr;
@@ -85,13 +94,41 @@ __device__ __forceinline__ u32x4 round8(const float acc[8]) {
   return as_u4(h);
 }
 
+// acc[u] += src[0][idx[u]] + src[1][idx[u]] + ... + src[n-1][idx[u]], added
+// in that order; the loads of up to NB sources are all issued first.
+template <int U, int NB>
+__device__ __forceinline__ void accumulate(float (&acc)[U][8], const f16* const* src, int n,
+                                           const int64_t (&idx)[U], const bool (&ok)[U]) {
+  for (int p0 = 0; p0 < n; p0 += NB) {
+    u32x4 v[NB][U];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (p0 + b < n) {
+        const f16* sp = src[p0 + b];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (ok[u]) v[b][u] = ld16_nt(sp + idx[u]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (p0 + b < n) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (ok[u]) add8(acc[u], v[b][u]);
+      }
+    }
+  }
+}
+
 // --------------------------------------------------------------- 2-D reduce
-// Unit (pm, cc): rows [pm*BM, +BM), columns [cc*comm_bn, +comm_bn) of the
-// (M x ncols) output; own values come from C at column offset col0.
+// Unit (pm, q, cc): rows [pm*BM + q*rows_u, +rows_u), columns
+// [cc*comm_bn, +comm_bn) of the (M x ncols) output; own values come from C
+// at column offset col0.
 template <int U>
-__device__ void reduce2d_unit(const CommArgs& a, int pm, int cc) {
-  const int r0 = pm * a.BM;
-  const int rows = min(a.BM, a.M - r0);
+__device__ void reduce2d_unit(const CommArgs& a, int pm, int q, int cc) {
+  const int r0 = pm * a.BM + q * a.rows_u;
+  const int rows = min(a.rows_u, a.M - r0);
   const int j0 = cc * a.comm_bn;
   const int cols = min(a.comm_bn, a.ncols - j0);
   if (rows <= 0 || cols <= 0) return;
@@ -102,6 +139,7 @@ __device__ void reduce2d_unit(const CommArgs& a, int pm, int cc) {
     float acc[U][8];
     int64_t orow[U];
     bool ok[U];
+    u32x4 own[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t i = base + u * kThreads;
@@ -110,19 +148,18 @@ __device__ void reduce2d_unit(const CommArgs& a, int pm, int cc) {
       const uint32_t c = i - r * vpr;
       orow[u] = (int64_t)(r0 + r) * a.ncols + j0 + c * 8;  // index into src/dst
       const int64_t cidx = (int64_t)(r0 + r) * a.ldc + a.col0 + j0 + c * 8;
+      if (ok[u]) own[u] = ld16(a.C + cidx);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[u][e] = 0.0f;
-      if (ok[u]) add8(acc[u], ld16(a.C + cidx));
+      if (ok[u]) add8(acc[u], own[u]);
     }
-    for (int p = 0; p < a.W; ++p) {
-      const f16* sp = a.src[p];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (ok[u]) add8(acc[u], ld16(sp + orow[u]));
-    }
+    accumulate<U, 8>(acc, a.src, a.W, orow, ok);
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (ok[u]) st16(a.dst + orow[u], round8(acc[u]));
+      if (ok[u]) st16_nt(a.dst + orow[u], round8(acc[u]));
   }
 }
 
@@ -136,22 +173,19 @@ __device__ void reduce_flat_unit(const CommArgs& a, int u) {
   const uint32_t total = (uint32_t)(n >> 3);
   for (uint32_t base = threadIdx.x; base < total; base += kThreads * U) {
     float acc[U][8];
+    int64_t idx[U];
     bool ok[U];
 #pragma unroll
     for (int v = 0; v < U; ++v) {
       ok[v] = base + v * kThreads < total;
+      idx[v] = e0 + (int64_t)(base + v * kThreads) * 8;
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[v][e] = 0.0f;
     }
-    for (int w = 0; w < a.W; ++w) {
-      const f16* sp = a.src[w] + e0;
-#pragma unroll
-      for (int v = 0; v < U; ++v)
-        if (ok[v]) add8(acc[v], ld16(sp + (int64_t)(base + v * kThreads) * 8));
-    }
+    accumulate<U, 8>(acc, a.src, a.W, idx, ok);
 #pragma unroll
     for (int v = 0; v < U; ++v)
-      if (ok[v]) st16(a.dst + e0 + (int64_t)(base + v * kThreads) * 8, round8(acc[v]));
+      if (ok[v]) st16_nt(a.dst + idx[v], round8(acc[v]));
   }
 }
 

@@ -57,6 +57,11 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds_addr, uint32_t of
 // ----------------------------------------------------------- plain vectors
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
+// streaming forms for data touched once (non-temporal cache policy)
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
+__device__ __forceinline__ void st16_nt(void* p, u32x4 v) { __builtin_nontemporal_store(v, (u32x4*)p); }
 
 __device__ __forceinline__ f16x8 as_h8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
 __device__ __forceinline__ u32x4 as_u4(f16x8 v) { return __builtin_bit_cast(u32x4, v); }

@@ -155,7 +155,7 @@ void save_cache_entry(const std::string& key, int value) {
 
 // --------------------------------------------------------------- config
 struct Resolved {
-  int bm, bn, bk, gm, gemm_wgs, comm_bn, comm_chunk, mode, flags;
+  int bm, bn, bk, gm, gemm_wgs, comm_bm, comm_bn, comm_chunk, mode, flags;
   int grid;
 };
 
@@ -184,6 +184,7 @@ int resolve_static(const iris_config_t* cfg, Resolved* r) {
   r->bk = c.block_k > 0 ? c.block_k : 64;
   r->gm = c.group_m > 0 ? c.group_m : kDefaultGroupM;
   r->gemm_wgs = c.gemm_wgs;
+  r->comm_bm = c.comm_block_m > 0 ? c.comm_block_m : 0;  // 0: chosen per op in run()
   r->comm_bn = c.comm_block_n > 0 ? c.comm_block_n : r->bn;
   r->comm_chunk = c.comm_chunk > 0 ? c.comm_chunk : kDefaultChunk;
   r->mode = c.mode;
@@ -193,6 +194,8 @@ int resolve_static(const iris_config_t* cfg, Resolved* r) {
                 r->bm, r->bn);
   if (r->bk != 64) return fail(IRIS_ERR_CONFIG, "block_k must be 64 (got %d)", r->bk);
   if (r->gm > 1 << 16) return fail(IRIS_ERR_CONFIG, "group_m too large (%d)", r->gm);
+  if (r->comm_bm > 0 && r->bm % r->comm_bm != 0)
+    return fail(IRIS_ERR_CONFIG, "comm_block_m must divide block_m (%d does not divide %d)", r->comm_bm, r->bm);
   if (r->comm_bn % 8 != 0) return fail(IRIS_ERR_CONFIG, "comm_block_n must be a multiple of 8 (got %d)", r->comm_bn);
   if (r->comm_chunk % 2048 != 0) return fail(IRIS_ERR_CONFIG, "comm_chunk must be a multiple of 2048 (got %d)", r->comm_chunk);
   if (r->mode != IRIS_MODE_FUSED && r->mode != IRIS_MODE_SEQUENTIAL)
@@ -222,13 +225,26 @@ int resolve_device(Resolved* r, int kind, const DevInfo& di, const std::string& 
   return IRIS_OK;
 }
 
+// Rows per comm unit when the config leaves it open: the largest power of
+// two dividing block_m that keeps a unit near a target size, 128 KiB of
+// shard for a copy unit and 32 KiB per buffer for a reduce unit. Units that
+// small let many workgroups share one GEMM row block, so the first blocks
+// are ready early, while each unit stays far above the cost of its claim
+// and release.
+int default_comm_rows(int kind, int bm, int64_t row_bytes) {
+  const int64_t target = kind == iris::OP_AG ? 131072 : 32768;
+  int rows = bm;
+  while (rows > 1 && (int64_t)rows * row_bytes > target) rows >>= 1;
+  return rows;
+}
+
 // ------------------------------------------------------------- workspace
 constexpr int kMaxGrid = iris::kMaxGrid;
 constexpr size_t kStampBytes = (size_t)kMaxGrid * 6 * sizeof(uint64_t);
 
 int64_t flag_words(int kind, int64_t M, int64_t N, int W, int bm, int bn) {
   const int64_t n_pm = (M + bm - 1) / bm, n_pn = (N + bn - 1) / bn;
-  if (kind == iris::OP_AG) return n_pm * W;
+  if (kind == iris::OP_AG) return n_pm * iris::kLine;
   if (kind == iris::OP_RS || kind == iris::OP_ARMM) return n_pm * n_pn;
   return 0;
 }
@@ -338,6 +354,13 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
       cache_key(di.arch, iris_op, d.M, d.N, d.kind == iris::OP_AG ? d.K_local : d.K, d.W, r.bm, r.bn, r.bk, r.gm);
   st = resolve_device(&r, d.kind, di, key);
   if (st) return st;
+  if (r.comm_bm <= 0) {
+    const int64_t row_bytes = d.kind == iris::OP_AG ? d.K_local * 2
+                              : d.kind == iris::OP_CONC_AR
+                                  ? 0
+                                  : std::min<int64_t>(r.comm_bn, d.kind == iris::OP_RS ? d.N / d.W : d.N) * 2;
+    r.comm_bm = default_comm_rows(d.kind, r.bm, row_bytes);
+  }
   if (used) *used = r;
 
   const int64_t words = flag_words(d.kind, d.M, d.N, d.W, r.bm, r.bn);
@@ -360,13 +383,17 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
   g.M = (int)d.M;
   g.N = (int)d.N;
   g.K = (int)d.K;
-  p.n_pm = (int)((d.M + r.bm - 1) / r.bm);
-  p.n_pn = (int)((d.N + r.bn - 1) / r.bn);
-  p.group_m = r.gm;
-  p.T_gemm = p.n_pm * p.n_pn;
+  const int n_pm = (int)((d.M + r.bm - 1) / r.bm);
+  const int n_pn = (int)((d.N + r.bn - 1) / r.bn);
+  p.order.n_pm = n_pm;
+  p.order.n_pn = n_pn;
+  p.order.group_m = r.gm;
+  p.T_gemm = n_pm * n_pn;
   iris::CommArgs& c = p.c;
   c.M = (int)d.M;
   c.BM = r.bm;
+  c.rows_u = r.comm_bm;
+  c.n_sub = r.bm / r.comm_bm;
   switch (d.kind) {
     case iris::OP_AG:
       c.W = d.W;
@@ -374,7 +401,7 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
       c.dst = (iris::f16*)d.out;
       c.K_local = d.K_local;
       c.K = d.K;
-      p.T_comm = p.n_pm * d.W;
+      p.T_comm = n_pm * d.W * c.n_sub;
       break;
     case iris::OP_RS:
     case iris::OP_ARMM: {
@@ -388,10 +415,10 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
       c.ncols = (int)nl;
       c.comm_bn = r.comm_bn;
       c.n_cc = (int)((nl + r.comm_bn - 1) / r.comm_bn);
-      p.T_comm = p.n_pm * c.n_cc;
+      p.T_comm = n_pm * c.n_sub * c.n_cc;
       // GEMM tiles feeding this rank's slice go first
-      p.prio_lo = c.col0 / r.bn;
-      p.prio_hi = (int)((c.col0 + nl + r.bn - 1) / r.bn);
+      p.order.prio_lo = c.col0 / r.bn;
+      p.order.prio_hi = (int)((c.col0 + nl + r.bn - 1) / r.bn);
       break;
     }
     case iris::OP_CONC_AR:

@@ -12,53 +12,28 @@
 // Dependencies of the dependent ops (Iris docs "Fused Communication and
 // Compute Operations": all_gather_matmul consumes the gathered A;
 // reduce_scatter / all_reduce consume A @ B + bias) are carried by ready
-// flags in the workspace:
-//   all_gather:  flag[pm*W + s] = 1 once shard s of row block pm is copied;
-//                a GEMM tile of row block pm waits for all W flags.
+// words in the workspace:
+//   all_gather:  rows[pm] counts the finished copy units of GEMM row block
+//                pm; a GEMM tile of that block waits until all W * n_sub
+//                are in. A second counter of all finished units lets a
+//                workgroup that has seen every unit done stop checking.
 //   reduce:      flag[pm*n_pn + pn] = 1 once GEMM tile (pm, pn) is stored;
 //                a reduce unit waits for the tiles covering its columns.
 // A workgroup that has to wait first takes unclaimed work from the queue it
 // waits on, so every wait ends even if not all workgroups are resident: a
 // claimed unit is always held by a running workgroup whose own work never
-// waits on the other queue.
+// waits on the other queue. A reduce unit whose tiles are all claimed only
+// spins: they are being computed, and taking another tile would hold the
+// reduce back by a whole tile.
 #include "launch.hpp"
 
 namespace iris {
 
-// ---------------------------------------------------------------- swizzle
-// t -> (pm, pn) on an n_pm x ncols grid, GROUP_M rows of tiles per group,
-// column-major inside a group.
-__device__ __forceinline__ void grouped(int t, int n_pm, int ncols, int gm, int& pm, int& pn) {
-  const int width = gm * ncols;
-  const int group = t / width;
-  const int first = group * gm;
-  const int gsz = min(gm, n_pm - first);
-  const int r = t - group * width;
-  pm = first + r % gsz;
-  pn = r / gsz;
-}
-
-// Column tiles [prio_lo, prio_hi) are visited first (all rows), then the rest.
-__device__ __forceinline__ void tile_coords(const Params& p, int t, int& pm, int& pn) {
-  const int np1 = p.prio_hi - p.prio_lo;
-  const int T1 = p.n_pm * np1;
-  int q;
-  if (t < T1) {
-    grouped(t, p.n_pm, np1, p.group_m, pm, q);
-    pn = p.prio_lo + q;
-  } else {
-    grouped(t - T1, p.n_pm, p.n_pn - np1, p.group_m, pm, q);
-    pn = q < p.prio_lo ? q : q + np1;
-  }
-}
-
 // ------------------------------------------------------------------ queues
+// One atomic per claim. A workgroup leaves a queue the first time it comes
+// back empty, so a counter overshoots its total by at most the grid size.
 __device__ __forceinline__ int claim(int* ctr, int T, int* slot) {
-  if (threadIdx.x == 0) {
-    int v = T;
-    if (ld_relaxed(ctr) < T) v = fetch_add(ctr, 1);
-    slot[0] = v;
-  }
+  if (threadIdx.x == 0) slot[0] = fetch_add(ctr, 1);
   __syncthreads();
   const int v = slot[0];
   __syncthreads();
@@ -68,12 +43,16 @@ __device__ __forceinline__ int claim(int* ctr, int T, int* slot) {
 // Release of a unit's results to other workgroups (any XCD): every wave
 // drains its stores to L2, the workgroup barriers, then one thread writes the
 // XCD's L2 back (agent-scope release fence), waits for that write-back to
-// finish, and only then sets the flag. The explicit wait matters: once the
-// stores are drained the compiler sees nothing outstanding and would issue
-// the flag store right behind the write-back.
-__device__ __forceinline__ void publish(int* flag) {
+// finish, and only then sets the flag (or bumps the counters). The explicit
+// wait matters: once the stores are drained the compiler sees nothing
+// outstanding and would issue the flag store right behind the write-back.
+__device__ __forceinline__ void release_begin() {
   drain_vmem();
   __syncthreads();
+}
+
+__device__ __forceinline__ void publish(int* flag) {
+  release_begin();
   if (threadIdx.x == 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     drain_vmem();
@@ -81,54 +60,101 @@ __device__ __forceinline__ void publish(int* flag) {
   }
 }
 
+__device__ __forceinline__ void publish_count(int* a, int* b) {
+  release_begin();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    drain_vmem();
+    fetch_add(a, 1);
+    fetch_add(b, 1);
+  }
+}
+
+// Pause between polls of a ready word, doubling from about 0.1 us to about
+// 1 us so that many waiting workgroups do not flood the line they poll.
+__device__ __forceinline__ void backoff(int& n) {
+  for (int i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(4);
+  n = n < 8 ? 2 * n : n;
+}
+
 // ------------------------------------------------------------ comm units
 template <int OP>
 __device__ void run_comm_unit(const Params& p, int u) {
+  const CommArgs& c = p.c;
   if constexpr (OP == OP_AG) {
-    const int pm = u / p.c.W;
-    ag_copy_unit<8>(p.c, pm, u - pm * p.c.W);
+    // u = (pm * W + s) * n_sub + q
+    const int per_block = c.W * c.n_sub;
+    const int pm = u / per_block;
+    const int r = u - pm * per_block;
+    const int s = r / c.n_sub;
+    ag_copy_unit<8>(c, pm, s, r - s * c.n_sub);
   } else if constexpr (OP == OP_RS || OP == OP_ARMM) {
-    const int pm = u / p.c.n_cc;
-    reduce2d_unit<2>(p.c, pm, u - pm * p.c.n_cc);
+    // u = (pm * n_sub + q) * n_cc + cc
+    const int slice = u / c.n_cc;
+    const int pm = slice / c.n_sub;
+    reduce2d_unit<2>(c, pm, slice - pm * c.n_sub, u - slice * c.n_cc);
   } else if constexpr (OP == OP_CONC_AR) {
-    reduce_flat_unit<2>(p.c, u);
+    reduce_flat_unit<2>(c, u);
+  }
+}
+
+__device__ __forceinline__ int ag_unit_block(const Params& p, int u) { return u / (p.c.W * p.c.n_sub); }
+
+// all_gather: the copy unit has landed; count it for its row block
+template <int OP>
+__device__ __forceinline__ void finish_comm_unit(const Params& p, int u) {
+  if constexpr (OP == OP_AG) {
+    if (p.fused) publish_count(p.ws + kFlagBase + ag_unit_block(p, u) * kLine, p.ws + kCommDone);
   }
 }
 
 template <int OP, class S>
-__device__ void run_gemm_tile(const Params& p, int t, int* slot, char* lds);
+__device__ void run_gemm_tile(const Params& p, int t, int* slot, char* lds, bool& rows_ready);
 
-// A GEMM tile of row block pm waits for the W shard copies of that block.
+// A GEMM tile of row block pm waits for the copy units of that block.
+// rows_ready: this workgroup has seen every copy unit finished (and has
+// acquired them), so no later tile needs to look.
 template <int OP, class S>
-__device__ void wait_rows(const Params& p, int pm, int* slot) {
-  const int* f = p.ws + kFlagBase + pm * p.c.W;
+__device__ void wait_rows(const Params& p, int pm, int* slot, bool& rows_ready) {
+  if (rows_ready) return;
+  const int* cnt = p.ws + kFlagBase + pm * kLine;
+  const int need = p.c.W * p.c.n_sub;
   uint32_t polls = 0;
+  int pause = 1;
+  bool comm_left = true;  // thread 0: the comm queue may still hold units
   while (true) {
     if (threadIdx.x == 0) {
-      int ready = 1, help = -1;
-      for (int s = 0; s < p.c.W; ++s)
-        if (ld_relaxed(f + s) == 0) { ready = 0; break; }
-      if (ready) {
-        fence_acquire();
-      } else if (ld_relaxed(p.ws + kCtrComm) < p.T_comm) {
-        const int u = fetch_add(p.ws + kCtrComm, 1);
+      int ready = 0, help = -1;
+      const int all = ld_relaxed(p.ws + kCommDone);
+      const int have = ld_relaxed(cnt);
+      if (all >= p.T_comm) {
+        ready = 2;
+      } else if (have >= need) {
+        ready = 1;
+      } else if (comm_left) {
+        const int u = ld_relaxed(p.ws + kCtrComm) < p.T_comm ? fetch_add(p.ws + kCtrComm, 1) : p.T_comm;
         if (u < p.T_comm) help = u;
+        else comm_left = false;
       } else if (++polls > p.spin_limit) {
         __hip_atomic_store(p.ws + kErr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         ready = 1;
       }
+      if (ready) fence_acquire();
       slot[0] = ready;
       slot[1] = help;
     }
     __syncthreads();
     const int ready = slot[0], help = slot[1];
     __syncthreads();
-    if (ready) return;
+    if (ready) {
+      rows_ready = ready == 2;
+      return;
+    }
     if (help >= 0) {
       run_comm_unit<OP>(p, help);
-      publish(p.ws + kFlagBase + help);
+      finish_comm_unit<OP>(p, help);
     } else {
-      __builtin_amdgcn_s_sleep(4);
+      backoff(pause);
     }
   }
 }
@@ -136,13 +162,18 @@ __device__ void wait_rows(const Params& p, int pm, int* slot) {
 // A reduce unit waits for the GEMM tiles covering its rows and columns.
 template <int OP, class S>
 __device__ void wait_tiles(const Params& p, int u, int* slot, char* lds) {
-  const int pm = u / p.c.n_cc;
-  const int cc = u - pm * p.c.n_cc;
+  const int pm = u / (p.c.n_cc * p.c.n_sub);
+  const int cc = u % p.c.n_cc;
   const int c_lo = p.c.col0 + cc * p.c.comm_bn;
   const int c_hi = min(c_lo + p.c.comm_bn, p.c.col0 + p.c.ncols);
   const int pn_lo = c_lo / S::BN, pn_hi = (c_hi - 1) / S::BN;
-  const int* f = p.ws + kFlagBase + pm * p.n_pn;
+  const int* f = p.ws + kFlagBase + pm * p.order.n_pn;
+  int last = 0;  // queue position of the last tile this unit needs
+  for (int pn = pn_lo; pn <= pn_hi; ++pn) last = max(last, tile_index(p.order, pm, pn));
+  bool rows_ready = false;  // unused by reduce ops
   uint32_t polls = 0;
+  int pause = 1;
+  bool deps_open = true;  // thread 0: some tile this unit needs may be unclaimed
   while (true) {
     if (threadIdx.x == 0) {
       int ready = 1, help = -1;
@@ -150,9 +181,10 @@ __device__ void wait_tiles(const Params& p, int u, int* slot, char* lds) {
         if (ld_relaxed(f + pn) == 0) { ready = 0; break; }
       if (ready) {
         fence_acquire();
-      } else if (ld_relaxed(p.ws + kCtrGemm) < p.T_gemm) {
-        const int t = fetch_add(p.ws + kCtrGemm, 1);
+      } else if (deps_open) {
+        const int t = ld_relaxed(p.ws + kCtrGemm) <= last ? fetch_add(p.ws + kCtrGemm, 1) : p.T_gemm;
         if (t < p.T_gemm) help = t;
+        else deps_open = false;
       } else if (++polls > p.spin_limit) {
         __hip_atomic_store(p.ws + kErr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         ready = 1;
@@ -165,23 +197,27 @@ __device__ void wait_tiles(const Params& p, int u, int* slot, char* lds) {
     __syncthreads();
     if (ready) return;
     if (help >= 0) {
-      run_gemm_tile<OP, S>(p, help, slot, lds);
+      run_gemm_tile<OP, S>(p, help, slot, lds, rows_ready);
     } else {
-      __builtin_amdgcn_s_sleep(4);
+      backoff(pause);
     }
   }
 }
 
 template <int OP, class S>
-__device__ void run_gemm_tile(const Params& p, int t, int* slot, char* lds) {
+__device__ void run_gemm_tile(const Params& p, int t, int* slot, char* lds, bool& rows_ready) {
   int pm, pn;
-  tile_coords(p, t, pm, pn);
+  tile_coords(p.order, t, pm, pn);
   if constexpr (OP == OP_AG) {
-    if (p.fused) wait_rows<OP, S>(p, pm, slot);
+    if (p.fused) wait_rows<OP, S>(p, pm, slot, rows_ready);
   }
   gemm_tile<S>(p.g, pm * S::BM, pn * S::BN, lds);
-  if constexpr (OP == OP_RS || OP == OP_ARMM) {
-    if (p.fused) publish(p.ws + kFlagBase + pm * p.n_pn + pn);
+  if constexpr (OP == OP_ARMM) {
+    if (p.fused) publish(p.ws + kFlagBase + pm * p.order.n_pn + pn);
+  } else if constexpr (OP == OP_RS) {
+    // only the columns of this rank's slice are consumed
+    if (p.fused && pn >= p.order.prio_lo && pn < p.order.prio_hi)
+      publish(p.ws + kFlagBase + pm * p.order.n_pn + pn);
   }
 }
 
@@ -192,6 +228,7 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char lds[S::LDS_BYTES];
   __shared__ int slot[2];
   uint64_t gs = ~0ull, ge = 0, cs = ~0ull, ce = 0;
+  bool rows_ready = false;
   const bool gemm_first = (int)blockIdx.x < p.gemm_wgs || p.T_comm == 0;
   for (int phase = 0; phase < 2; ++phase) {
     if (phase == 1 && !p.steal) break;
@@ -202,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(Params p) {
         if (t < 0) break;
         const uint64_t t0 = stamp_now();
         gs = t0 < gs ? t0 : gs;
-        run_gemm_tile<OP, S>(p, t, slot, lds);
+        run_gemm_tile<OP, S>(p, t, slot, lds, rows_ready);
         ge = stamp_now();
       }
     } else {
@@ -215,9 +252,7 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(Params p) {
         const uint64_t t0 = stamp_now();
         cs = t0 < cs ? t0 : cs;
         run_comm_unit<OP>(p, u);
-        if constexpr (OP == OP_AG) {
-          if (p.fused) publish(p.ws + kFlagBase + u);
-        }
+        finish_comm_unit<OP>(p, u);
         ce = stamp_now();
       }
     }

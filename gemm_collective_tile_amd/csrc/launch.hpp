@@ -7,6 +7,7 @@
 
 #include "comm_units.hpp"
 #include "gemm_tile.hpp"
+#include "schedule.hpp"
 
 namespace iris {
 
@@ -21,21 +22,27 @@ enum OpKind : int32_t {
 // Workspace layout: first uint64 stamps[kMaxGrid][4] written by the
 // persistent kernel and uint64 comm_stamps[kMaxGrid][2] written by the
 // sequential-mode comm kernel (a fixed-size block), then the int32 words
-//   [0] GEMM queue counter   [1] comm queue counter   [2] error word (sticky)
-//   [3] finished-workgroup counter                    [kFlagBase ...] ready flags
+//   GEMM queue counter, comm queue counter, error word (sticky), finished-
+//   workgroup counter, finished comm units (all_gather), then from kFlagBase
+//   the ready words: all_gather, one counter per GEMM row block (finished
+//   copy units of that block, kLine words apart); reduce, one flag per GEMM
+//   tile
 // Every word but the error word is zero when a persistent launch starts; the
 // last workgroup to finish zeroes them again, so consecutive ops on one
 // workspace need no separate reset.
-constexpr int kCtrGemm = 0, kCtrComm = 1, kErr = 2, kDone = 3;
-constexpr int kFlagBase = 16;
+// Each counter sits on its own 128-byte line (kLine words), and so does each
+// all_gather row-block counter: many workgroups poll these while others bump
+// them, and words sharing a line would serialise both.
+constexpr int kLine = 32;
+constexpr int kCtrGemm = 0, kCtrComm = kLine, kErr = 2 * kLine, kDone = 3 * kLine, kCommDone = 4 * kLine;
+constexpr int kFlagBase = 5 * kLine;
 constexpr int kMaxGrid = 2048;
 
 struct Params {
   GemmArgs g;
   CommArgs c;
   int32_t op;
-  int32_t n_pm, n_pn, group_m;
-  int32_t prio_lo, prio_hi;  // GEMM column tiles [prio_lo, prio_hi) go first
+  TileOrder order;           // GEMM tile grid and visiting order
   int32_t T_gemm, T_comm;
   int32_t gemm_wgs;          // pid < gemm_wgs starts on the GEMM queue
   int32_t steal;             // switch to the other queue when the first is empty

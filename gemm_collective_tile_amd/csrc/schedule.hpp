@@ -1,0 +1,59 @@
+// Order in which GEMM tiles leave the work queue, and its inverse.
+//
+// Tiles are visited in GROUP_M-grouped order (iris.concurrent PR, the
+// commits that keep the GROUP_M work-stealing tile swizzle): GROUP_M rows of
+// tiles form a group, visited column by column, so consecutive tiles share
+// B columns and a few A row blocks in L2. Column tiles [prio_lo, prio_hi)
+// (the ones a reduce_scatter unit of this rank consumes) are visited first,
+// all rows, then the rest in the same grouped order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace iris {
+
+struct TileOrder {
+  int n_pm, n_pn, group_m;
+  int prio_lo, prio_hi;
+};
+
+// t -> (pm, pn) on an n_pm x ncols grid.
+__host__ __device__ inline void grouped(int t, int n_pm, int ncols, int gm, int& pm, int& pn) {
+  const int width = gm * ncols;
+  const int group = t / width;
+  const int first = group * gm;
+  const int gsz = n_pm - first < gm ? n_pm - first : gm;
+  const int r = t - group * width;
+  pm = first + r % gsz;
+  pn = r / gsz;
+}
+
+// (pm, pn) -> t, the inverse of grouped().
+__host__ __device__ inline int grouped_index(int pm, int pn, int n_pm, int ncols, int gm) {
+  const int group = pm / gm;
+  const int first = group * gm;
+  const int gsz = n_pm - first < gm ? n_pm - first : gm;
+  return group * gm * ncols + pn * gsz + (pm - first);
+}
+
+__host__ __device__ inline void tile_coords(const TileOrder& o, int t, int& pm, int& pn) {
+  const int np1 = o.prio_hi - o.prio_lo;
+  const int T1 = o.n_pm * np1;
+  int q;
+  if (t < T1) {
+    grouped(t, o.n_pm, np1, o.group_m, pm, q);
+    pn = o.prio_lo + q;
+  } else {
+    grouped(t - T1, o.n_pm, o.n_pn - np1, o.group_m, pm, q);
+    pn = q < o.prio_lo ? q : q + np1;
+  }
+}
+
+__host__ __device__ inline int tile_index(const TileOrder& o, int pm, int pn) {
+  const int np1 = o.prio_hi - o.prio_lo;
+  if (pn >= o.prio_lo && pn < o.prio_hi) return grouped_index(pm, pn - o.prio_lo, o.n_pm, np1, o.group_m);
+  const int q = pn < o.prio_lo ? pn : pn - np1;
+  return o.n_pm * np1 + grouped_index(pm, q, o.n_pm, o.n_pn - np1, o.group_m);
+}
+
+}  // namespace iris

@@ -104,6 +104,11 @@ typedef enum iris_status {
  *   group_m           rows of tiles per swizzle group. Default 8.
  *   gemm_wgs          workgroups that start on the GEMM queue in fused mode,
  *                     1..G-1 where G = iris_grid_size(). Default 7/8 of G.
+ *   comm_block_m      rows per comm unit (all_gather copy and the
+ *                     reduce of reduce_scatter / matmul_all_reduce); must
+ *                     divide block_m. Default: the largest power of two
+ *                     dividing block_m that keeps a unit near 128 KiB of
+ *                     shard (copy) or 32 KiB per buffer (reduce).
  *   comm_block_n      columns per reduce unit (reduce_scatter and
  *                     matmul_all_reduce), multiple of 8. Default block_n.
  *   comm_chunk        elements per all_reduce unit of iris_concurrent,
@@ -117,6 +122,7 @@ typedef struct iris_config {
   int32_t block_k;
   int32_t group_m;
   int32_t gemm_wgs;
+  int32_t comm_block_m;
   int32_t comm_block_n;
   int32_t comm_chunk;
   int32_t mode;

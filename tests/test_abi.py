@@ -107,7 +107,7 @@ def test_config_errors_before_any_device_call(lib):
     shards = ptrs(2)
     for cfg, code in [(Config(block_m=96, block_n=96), 3), (Config(block_k=32), 3),
                       (Config(mode=7), 3), (Config(flags=64), 3), (Config(comm_block_n=12), 3),
-                      (Config(comm_chunk=1000), 3)]:
+                      (Config(comm_chunk=1000), 3), (Config(comm_block_m=96), 3)]:
         c = ctypes.pointer(cfg._c())
         assert lib.iris_ag_mm(P, P, shards, 2, P, None, 256, 256, 256, c, None, 0, None) == code, cfg
 
@@ -118,9 +118,12 @@ def test_workspace_size_is_host_only(lib):
     a = iris_workspace_size(IRIS_OP_AG_MM, 131072, 16384, 2048, 8)
     r = iris_workspace_size(IRIS_OP_MM_RS, 4096, 11008, 4096, 8)
     c = iris_workspace_size(IRIS_OP_CONCURRENT, 8192, 8192, 8192, 8)
-    assert a > r > 0 and c > 0
-    # AG flags: ceil(M/256) row blocks x W shards; RS flags: row blocks x column tiles
-    assert a - c >= 512 * 8 * 4
+    assert a > c > 0 and r > c
+    # AG: one ready counter per row block (ceil(M/256)), each on its own
+    # 128-byte line; RS: one flag per GEMM tile (16 x 43); concurrent: none
+    # (the fixed counter words and the 256-byte rounding are in all three)
+    assert a - c >= 512 * 128 - 256
+    assert r - c >= 16 * 43 * 4 - 256
     assert iris_workspace_size(99, 1, 1, 1, 1) == 0
     assert iris_workspace_size(IRIS_OP_AG_MM, 0, 8, 8, 1) == 0
 

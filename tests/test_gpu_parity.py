@@ -131,6 +131,26 @@ def test_ag_w1_equals_plain_gemm():
     assert_bits_equal(C, C2, "W=1 all_gather_matmul vs plain GEMM")
 
 
+def test_ag_comm_rows_variants():
+    """Copy units of 1 row up to a whole row block (M = 300 leaves a ragged
+    last block and empty units): the gathered matrix is bit-exact and C is
+    bit-identical whatever the unit size and split."""
+    inp = ag_inputs(300, 200, 40, 3, seed=13)
+    g_ref, c_ref = oracle_ag(inp)
+    G = il.iris_grid_size(Config(block_m=64, block_n=64))
+    first = {}
+    for tile, rows, gw in [((64, 64), 1, 0), ((64, 64), 8, 1), ((64, 64), 64, G - 1), ((256, 256), 1, 0),
+                           ((256, 256), 16, 4), ((256, 256), 256, 0), ((256, 128), 32, 0)]:
+        note(f"ag_mm tile={tile} comm_block_m={rows} gemm_wgs={gw}")
+        C, Gb = run_ag(inp, Config(block_m=tile[0], block_n=tile[1], comm_block_m=rows, gemm_wgs=gw))
+        assert_bits_equal(Gb, g_ref, f"gathered rows={rows}")
+        assert_close(C, c_ref, f"C rows={rows}")
+        if tile in first:
+            assert_bits_equal(C, first[tile], f"C invariant under comm_block_m={rows} gemm_wgs={gw}")
+        else:
+            first[tile] = C
+
+
 # ----------------------------------------------------------- reduce_scatter
 
 def rs_inputs(M, N, K, W, seed=0, integer=False, zero_partials=False):
@@ -179,6 +199,26 @@ def test_mm_rs_integer_exact_and_zero_partials():
     z = rs_inputs(M, N, K, W, seed=7, zero_partials=True)
     out, C = run_rs(z, W, 2)
     assert_bits_equal(out, C[:, 2 * (N // W):3 * (N // W)].contiguous(), "zero partials -> own slice")
+
+
+def test_mm_rs_comm_rows_variants():
+    """Reduce units from 1 row x 8 columns to a whole row block; the slice
+    is bit-identical across unit shapes, gemm_wgs and modes."""
+    W, M, N, K = 4, 300, 800, 136
+    inp = rs_inputs(M, N, K, W, seed=14)
+    ref = oracle.matmul_reduce_scatter(host(inp["A"]), host(inp["B"]), [host(p) for p in inp["partials"]],
+                                       W, rank=2, bias=host(inp["bias"]))
+    G = il.iris_grid_size(Config(block_m=64, block_n=64))
+    first = None
+    for rows, cols, gw, mode in [(1, 8, 0, 0), (8, 64, 1, 0), (64, 200, G - 1, 0), (16, 24, 0, 1), (4, 200, 3, 0)]:
+        note(f"mm_rs comm_block_m={rows} comm_block_n={cols} gemm_wgs={gw} mode={mode}")
+        out, _ = run_rs(inp, W, 2, Config(block_m=64, block_n=64, comm_block_m=rows, comm_block_n=cols,
+                                          gemm_wgs=gw, mode=mode))
+        assert_close(out, ref, f"out rows={rows} cols={cols}")
+        if first is None:
+            first = out
+        else:
+            assert_bits_equal(out, first, f"out invariant rows={rows} cols={cols} gemm_wgs={gw}")
 
 
 def test_mm_rs_w1_and_partial_permutation():
