@@ -84,7 +84,7 @@ class Case:
             self.op = il.IRIS_OP_CONCURRENT
         else:
             raise ValueError(w.op)
-        self.G_wgs = il.iris_grid_size(None)
+        self.G_wgs = il.iris_grid_size(None, op=self.op)
 
     def step(self, cfg):
         il, w, inp = self.il, self.w, self.inp

@@ -105,7 +105,7 @@ def _load() -> ctypes.CDLL:
         "iris_mm_rs_local": [vp, vp, vp, vp, vp, vpp, i32, i32, i64, i64, i64, cfgp, vp, sz, vp],
         "iris_mm_ar_local": [vp, vp, vp, vp, vp, vpp, i32, i64, i64, i64, cfgp, vp, sz, vp],
         "iris_concurrent": [vp, vp, vp, vp, i64, i64, i64, i32, vp, vpp, i32, i64, cfgp, vp, sz, vp],
-        "iris_grid_size": [cfgp],
+        "iris_grid_size": [ctypes.c_int32, cfgp],
         "iris_tune_gemm_wgs": [ctypes.POINTER(_OpArgs), ctypes.POINTER(i32), i32, i32,
                                ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float), vp],
         "iris_last_windows": [vp, vp] + [ctypes.POINTER(ctypes.c_double)] * 4,
@@ -237,8 +237,9 @@ def iris_workspace_size(op, M, N, K, W, config=None) -> int:
     return int(_lib.iris_workspace_size(op, M, N, K, W, _cfg(config)))
 
 
-def iris_grid_size(config=None) -> int:
-    g = _lib.iris_grid_size(_cfg(config))
+def iris_grid_size(config=None, op=IRIS_OP_AG_MM) -> int:
+    """Workgroups of the fused persistent launch of `op` for this config."""
+    g = _lib.iris_grid_size(op, _cfg(config))
     if g < 0:
         _check(-g)
     return g

@@ -51,8 +51,11 @@ struct CommArgs {
 };
 
 // ------------------------------------------------------------- all_gather
-// Unit (pm, s, q): rows [pm*BM + q*rows_u, +rows_u) of shard s.
-template <int U>
+// Unit (pm, s, q): rows [pm*BM + q*rows_u, +rows_u) of shard s. COHERENT:
+// store with the agent-coherent policy, so the unit can be published without
+// an L2 write-back (the fused op); the sequential copy kernel uses plain
+// stores.
+template <int U, bool COHERENT>
 __device__ void ag_copy_unit(const CommArgs& a, int pm, int s, int q) {
   const int r0 = pm * a.BM + q * a.rows_u;
   const int rows = min(a.rows_u, a.M - r0);
@@ -62,6 +65,9 @@ __device__ void ag_copy_unit(const CommArgs& a, int pm, int s, int q) {
   const FastDiv fd = FastDiv::make(vpr);
   const f16* src = a.src[s] + (int64_t)r0 * a.K_local;  // rows are contiguous
   f16* dst = a.dst + (int64_t)r0 * a.K + (int64_t)s * a.K_local;
+  // the unit's stores span (rows - 1) * K + K_local elements from dst; the
+  // host keeps rows_u * K * 2 below 2^31 bytes
+  const auto rdst = make_rsrc(dst, (uint32_t)(((int64_t)(rows - 1) * a.K + a.K_local) * 2));
   for (uint32_t base = threadIdx.x; base < total; base += kThreads * U) {
     u32x4 v[U];
 #pragma unroll
@@ -75,7 +81,10 @@ __device__ void ag_copy_unit(const CommArgs& a, int pm, int s, int q) {
       if (i < total) {
         const uint32_t r = fd.div(i);
         const uint32_t c = i - r * vpr;
-        st16(dst + (int64_t)r * a.K + c * 8, v[u]);
+        if constexpr (COHERENT)
+          buf_store16_coherent(rdst, (uint32_t)(((int64_t)r * a.K + c * 8) * 2), v[u]);
+        else
+          st16(dst + (int64_t)r * a.K + c * 8, v[u]);
       }
     }
   }

@@ -35,6 +35,15 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+// Agent-coherent 16-byte store (sc1 cache policy): the write goes through
+// the XCD's L2, so once this wave's vmcnt reaches zero the data is visible
+// to every XCD and no L2 write-back is needed before a flag that publishes
+// it (agent-scope relaxed atomic stores use the same policy).
+constexpr int kPolicySc1 = 16;
+__device__ __forceinline__ void buf_store16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kPolicySc1);
+}
+
 // The same resource as four dwords, for use as an inline-asm operand.
 __device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
   const uint64_t a = (uint64_t)base;

@@ -360,7 +360,13 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
                                   ? 0
                                   : std::min<int64_t>(r.comm_bn, d.kind == iris::OP_RS ? d.N / d.W : d.N) * 2;
     r.comm_bm = default_comm_rows(d.kind, r.bm, row_bytes);
+    while (d.kind == iris::OP_AG && r.comm_bm > 1 && (int64_t)r.comm_bm * d.K * 2 >= (int64_t)1 << 31)
+      r.comm_bm >>= 1;
   }
+  // a copy unit addresses its gathered rows through one 32-bit buffer range
+  if (d.kind == iris::OP_AG && (int64_t)r.comm_bm * d.K * 2 >= (int64_t)1 << 31)
+    return fail(IRIS_ERR_CONFIG, "comm_block_m %d times the gathered row (%lld bytes) exceeds 2 GiB", r.comm_bm,
+                (long long)(d.K * 2));
   if (used) *used = r;
 
   const int64_t words = flag_words(d.kind, d.M, d.N, d.W, r.bm, r.bn);
@@ -388,8 +394,12 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
   p.order.n_pm = n_pm;
   p.order.n_pn = n_pn;
   p.order.group_m = r.gm;
+  if ((int64_t)n_pm * n_pn > (1 << 30))
+    return fail(IRIS_ERR_UNSUPPORTED, "too many GEMM tiles (%lld; limit 2^30)", (long long)n_pm * n_pn);
   p.T_gemm = n_pm * n_pn;
+  p.xcd_q = std::max(1, r.grid / iris::kXcds);
   iris::CommArgs& c = p.c;
+  int64_t t_comm = 0;
   c.M = (int)d.M;
   c.BM = r.bm;
   c.rows_u = r.comm_bm;
@@ -401,7 +411,7 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
       c.dst = (iris::f16*)d.out;
       c.K_local = d.K_local;
       c.K = d.K;
-      p.T_comm = n_pm * d.W * c.n_sub;
+      t_comm = (int64_t)n_pm * d.W * c.n_sub;
       break;
     case iris::OP_RS:
     case iris::OP_ARMM: {
@@ -415,7 +425,7 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
       c.ncols = (int)nl;
       c.comm_bn = r.comm_bn;
       c.n_cc = (int)((nl + r.comm_bn - 1) / r.comm_bn);
-      p.T_comm = n_pm * c.n_sub * c.n_cc;
+      t_comm = (int64_t)n_pm * c.n_sub * c.n_cc;
       // GEMM tiles feeding this rank's slice go first
       p.order.prio_lo = c.col0 / r.bn;
       p.order.prio_hi = (int)((c.col0 + nl + r.bn - 1) / r.bn);
@@ -427,9 +437,12 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
       c.dst = (iris::f16*)d.out;
       c.elems = d.comm_elems;
       c.chunk = r.comm_chunk;
-      p.T_comm = (int)((d.comm_elems + r.comm_chunk - 1) / r.comm_chunk);
+      t_comm = (d.comm_elems + r.comm_chunk - 1) / r.comm_chunk;
       break;
   }
+  if (t_comm > (1 << 30))
+    return fail(IRIS_ERR_UNSUPPORTED, "too many comm units (%lld; limit 2^30)", (long long)t_comm);
+  p.T_comm = (int)t_comm;
   // Layout: the timestamp block at a fixed offset 0, then the counters and
   // flags. The flag region's size depends on the op; with the stamps first,
   // no op's stamps can land on another op's flag words.
@@ -627,7 +640,10 @@ size_t iris_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32_t 
   return int_region_bytes(flag_words(kind, M, N, W, r.bm, r.bn)) + kStampBytes;
 }
 
-int iris_grid_size(const iris_config_t* cfg) {
+int iris_grid_size(int32_t op, const iris_config_t* cfg) {
+  g_msg.clear();
+  const int kind = iris_op_to_kind(op);
+  if (kind < 0) return -fail(IRIS_ERR_INVALID_ARG, "unknown op %d", op);
   Resolved r{};
   int st = resolve_static(cfg, &r);
   if (st) return -st;
@@ -635,7 +651,7 @@ int iris_grid_size(const iris_config_t* cfg) {
   DevInfo di;
   st = current_device(&dev, &di);
   if (st) return -st;
-  const int occ = iris::persistent_blocks_per_cu(r.bm, r.bn, iris::OP_AG);
+  const int occ = iris::persistent_blocks_per_cu(r.bm, r.bn, kind);
   if (occ <= 0) return -fail(IRIS_ERR_HIP, "occupancy query failed");
   return std::min(di.cus * occ, kMaxGrid);
 }
@@ -650,7 +666,7 @@ int iris_tune_gemm_wgs(const iris_op_args_t* a, const int32_t* candidates, int32
   iris_config_t cfg = a->cfg;
   cfg.mode = IRIS_MODE_FUSED;
   // the static default is always benchmarked, so tuning never loses to it
-  int G = iris_grid_size(&cfg);
+  int G = iris_grid_size(a->op, &cfg);
   if (G < 0) return -G;
   std::vector<int> cands(candidates, candidates + n_candidates);
   const int def = (G * 7) / 8;

@@ -40,6 +40,34 @@ __device__ __forceinline__ int claim(int* ctr, int T, int* slot) {
   return v < T ? v : -1;
 }
 
+// The XCD this workgroup runs on (hardware XCC_ID register).
+__device__ __forceinline__ int xcd_id() {
+  return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (15 << 11)) & (kXcds - 1);
+}
+
+// GEMM claim: this XCD's queue first, then the others in turn. `gone`
+// (meaningful in thread 0) marks queues this workgroup has seen empty, so
+// each queue's counter overshoots its share by at most one per workgroup.
+__device__ __forceinline__ int claim_gemm(const Params& p, int home, uint32_t& gone, int* slot) {
+  if (threadIdx.x == 0) {
+    int t = -1;
+    for (int i = 0; i < kXcds && t < 0; ++i) {
+      const int x = (home + i) & (kXcds - 1);
+      if (gone & (1u << x)) continue;
+      const int c = xcd_tile(p.xcd_q, x, fetch_add(p.ws + kCtrGemm + x * kLine, 1));
+      if (c < p.T_gemm)
+        t = c;
+      else
+        gone |= 1u << x;
+    }
+    slot[0] = t;
+  }
+  __syncthreads();
+  const int v = slot[0];
+  __syncthreads();
+  return v;
+}
+
 // Release of a unit's results to other workgroups (any XCD): every wave
 // drains its stores to L2, the workgroup barriers, then one thread writes the
 // XCD's L2 back (agent-scope release fence), waits for that write-back to
@@ -60,11 +88,12 @@ __device__ __forceinline__ void publish(int* flag) {
   }
 }
 
-__device__ __forceinline__ void publish_count(int* a, int* b) {
+// For data written with agent-coherent stores (buf_store16_coherent): once
+// every wave's stores have completed they are visible on every XCD, so the
+// counters can be bumped with no L2 write-back in between.
+__device__ __forceinline__ void publish_count_coherent(int* a, int* b) {
   release_begin();
   if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    drain_vmem();
     fetch_add(a, 1);
     fetch_add(b, 1);
   }
@@ -78,7 +107,7 @@ __device__ __forceinline__ void backoff(int& n) {
 }
 
 // ------------------------------------------------------------ comm units
-template <int OP>
+template <int OP, bool FUSED = true>
 __device__ void run_comm_unit(const Params& p, int u) {
   const CommArgs& c = p.c;
   if constexpr (OP == OP_AG) {
@@ -87,7 +116,7 @@ __device__ void run_comm_unit(const Params& p, int u) {
     const int pm = u / per_block;
     const int r = u - pm * per_block;
     const int s = r / c.n_sub;
-    ag_copy_unit<8>(c, pm, s, r - s * c.n_sub);
+    ag_copy_unit<8, FUSED>(c, pm, s, r - s * c.n_sub);
   } else if constexpr (OP == OP_RS || OP == OP_ARMM) {
     // u = (pm * n_sub + q) * n_cc + cc
     const int slice = u / c.n_cc;
@@ -104,7 +133,7 @@ __device__ __forceinline__ int ag_unit_block(const Params& p, int u) { return u 
 template <int OP>
 __device__ __forceinline__ void finish_comm_unit(const Params& p, int u) {
   if constexpr (OP == OP_AG) {
-    if (p.fused) publish_count(p.ws + kFlagBase + ag_unit_block(p, u) * kLine, p.ws + kCommDone);
+    if (p.fused) publish_count_coherent(p.ws + kFlagBase + ag_unit_block(p, u) * kLine, p.ws + kCommDone);
   }
 }
 
@@ -168,8 +197,6 @@ __device__ void wait_tiles(const Params& p, int u, int* slot, char* lds) {
   const int c_hi = min(c_lo + p.c.comm_bn, p.c.col0 + p.c.ncols);
   const int pn_lo = c_lo / S::BN, pn_hi = (c_hi - 1) / S::BN;
   const int* f = p.ws + kFlagBase + pm * p.order.n_pn;
-  int last = 0;  // queue position of the last tile this unit needs
-  for (int pn = pn_lo; pn <= pn_hi; ++pn) last = max(last, tile_index(p.order, pm, pn));
   bool rows_ready = false;  // unused by reduce ops
   uint32_t polls = 0;
   int pause = 1;
@@ -182,9 +209,19 @@ __device__ void wait_tiles(const Params& p, int u, int* slot, char* lds) {
       if (ready) {
         fence_acquire();
       } else if (deps_open) {
-        const int t = ld_relaxed(p.ws + kCtrGemm) <= last ? fetch_add(p.ws + kCtrGemm, 1) : p.T_gemm;
-        if (t < p.T_gemm) help = t;
-        else deps_open = false;
+        // a needed tile still in its XCD queue: take work from that queue
+        int hx = -1;
+        for (int pn = pn_lo; pn <= pn_hi && hx < 0; ++pn) {
+          int x, j;
+          xcd_slot(p.xcd_q, tile_index(p.order, pm, pn), x, j);
+          if (ld_relaxed(p.ws + kCtrGemm + x * kLine) <= j) hx = x;
+        }
+        if (hx < 0) {
+          deps_open = false;
+        } else {
+          const int t = xcd_tile(p.xcd_q, hx, fetch_add(p.ws + kCtrGemm + hx * kLine, 1));
+          if (t < p.T_gemm) help = t;
+        }
       } else if (++polls > p.spin_limit) {
         __hip_atomic_store(p.ws + kErr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         ready = 1;
@@ -229,13 +266,15 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(Params p) {
   __shared__ int slot[2];
   uint64_t gs = ~0ull, ge = 0, cs = ~0ull, ce = 0;
   bool rows_ready = false;
+  const int home = xcd_id();
+  uint32_t gone = 0;
   const bool gemm_first = (int)blockIdx.x < p.gemm_wgs || p.T_comm == 0;
   for (int phase = 0; phase < 2; ++phase) {
     if (phase == 1 && !p.steal) break;
     const bool do_gemm = (phase == 0) == gemm_first;
     if (do_gemm) {
       while (true) {
-        const int t = claim(p.ws + kCtrGemm, p.T_gemm, slot);
+        const int t = claim_gemm(p, home, gone, slot);
         if (t < 0) break;
         const uint64_t t0 = stamp_now();
         gs = t0 < gs ? t0 : gs;
@@ -281,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void comm_only_kernel(Params p) {
   uint64_t cs = ~0ull, ce = 0;
   for (int u = blockIdx.x; u < p.T_comm; u += gridDim.x) {
     if (cs == ~0ull) cs = stamp_now();
-    run_comm_unit<OP>(p, u);
+    run_comm_unit<OP, false>(p, u);
     ce = stamp_now();
   }
   if (threadIdx.x == 0) {

@@ -22,7 +22,7 @@ enum OpKind : int32_t {
 // Workspace layout: first uint64 stamps[kMaxGrid][4] written by the
 // persistent kernel and uint64 comm_stamps[kMaxGrid][2] written by the
 // sequential-mode comm kernel (a fixed-size block), then the int32 words
-//   GEMM queue counter, comm queue counter, error word (sticky), finished-
+//   GEMM queue counters (one per XCD), comm queue counter, error word (sticky), finished-
 //   workgroup counter, finished comm units (all_gather), then from kFlagBase
 //   the ready words: all_gather, one counter per GEMM row block (finished
 //   copy units of that block, kLine words apart); reduce, one flag per GEMM
@@ -34,8 +34,10 @@ enum OpKind : int32_t {
 // all_gather row-block counter: many workgroups poll these while others bump
 // them, and words sharing a line would serialise both.
 constexpr int kLine = 32;
-constexpr int kCtrGemm = 0, kCtrComm = kLine, kErr = 2 * kLine, kDone = 3 * kLine, kCommDone = 4 * kLine;
-constexpr int kFlagBase = 5 * kLine;
+constexpr int kCtrGemm = 0;  // kXcds GEMM queue counters, one line each
+constexpr int kCtrComm = kXcds * kLine, kErr = kCtrComm + kLine, kDone = kErr + kLine,
+              kCommDone = kDone + kLine;
+constexpr int kFlagBase = kCommDone + kLine;
 constexpr int kMaxGrid = 2048;
 
 struct Params {
@@ -43,6 +45,7 @@ struct Params {
   CommArgs c;
   int32_t op;
   TileOrder order;           // GEMM tile grid and visiting order
+  int32_t xcd_q;             // tiles per block dealt to each XCD queue
   int32_t T_gemm, T_comm;
   int32_t gemm_wgs;          // pid < gemm_wgs starts on the GEMM queue
   int32_t steal;             // switch to the other queue when the first is empty

@@ -56,4 +56,28 @@ __host__ __device__ inline int tile_index(const TileOrder& o, int pm, int pn) {
   return o.n_pm * np1 + grouped_index(pm, q, o.n_pm, o.n_pn - np1, o.group_m);
 }
 
+// ------------------------------------------------------- per-XCD queues
+// MI355X has 8 XCDs, each with its own L2, and hands workgroups to them
+// round-robin. The tile sequence above is dealt to one queue per XCD in
+// blocks of Q consecutive tiles: block b goes to XCD b mod 8. With Q about
+// the number of workgroups an XCD holds, the tiles an XCD runs at once form
+// one compact patch of the grouped order (at Q = 32 and GROUP_M = 8, 8 row
+// blocks x 4 column tiles), so their A rows and B columns meet in that XCD's
+// L2 instead of being fetched by all eight.
+constexpr int kXcds = 8;
+
+// j-th tile of XCD x's queue -> position in the tile sequence. Increasing in
+// j, so the queue holds exactly the j with xcd_tile(...) < T.
+__host__ __device__ inline int xcd_tile(int Q, int x, int j) {
+  const int blk = j / Q;
+  return (blk * kXcds + x) * Q + (j - blk * Q);
+}
+
+// position t -> (XCD queue x, index j in it), the inverse of xcd_tile().
+__host__ __device__ inline void xcd_slot(int Q, int t, int& x, int& j) {
+  const int b = t / Q;
+  x = b % kXcds;
+  j = (b / kXcds) * Q + (t - b * Q);
+}
+
 }  // namespace iris

@@ -103,7 +103,8 @@ typedef enum iris_status {
  *   block_k           K step; 64 only. Default 64.
  *   group_m           rows of tiles per swizzle group. Default 8.
  *   gemm_wgs          workgroups that start on the GEMM queue in fused mode,
- *                     1..G-1 where G = iris_grid_size(). Default 7/8 of G.
+ *                     1..G-1 where G = iris_grid_size(op, cfg). Default
+ *                     7/8 of G.
  *   comm_block_m      rows per comm unit (all_gather copy and the
  *                     reduce of reduce_scatter / matmul_all_reduce); must
  *                     divide block_m. Default: the largest power of two
@@ -194,9 +195,10 @@ int iris_concurrent(void* C, const void* A, const void* B, const void* bias,
 size_t iris_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32_t W,
                            const iris_config_t* cfg);
 
-/* Persistent grid size G (workgroups) the fused kernels launch on the
- * current device for this config, or a negative iris_status. */
-int iris_grid_size(const iris_config_t* cfg);
+/* Persistent grid size G (workgroups) the fused kernel of `op` (IRIS_OP_*)
+ * launches on the current device for this config: CUs times the
+ * workgroups of that kernel resident per CU. Negative iris_status on error. */
+int iris_grid_size(int32_t op, const iris_config_t* cfg);
 
 /*
  * Host-side CU-split sweep ([PR544]: benchmark candidates, always including

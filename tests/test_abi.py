@@ -134,3 +134,9 @@ def test_python_binding_rejects_cpu_tensors():
     x = torch.zeros(8, 8, dtype=torch.float16)
     with pytest.raises((ValueError, TypeError)):
         iris_ag_mm(x, x, [x], x)
+
+
+def test_grid_size_rejects_unknown_op(lib):
+    # the op is checked before the device is queried
+    assert lib.iris_grid_size(99, None) == -1
+    assert "unknown op" in lib.iris_last_error_message().decode()

@@ -208,7 +208,7 @@ def test_mm_rs_comm_rows_variants():
     inp = rs_inputs(M, N, K, W, seed=14)
     ref = oracle.matmul_reduce_scatter(host(inp["A"]), host(inp["B"]), [host(p) for p in inp["partials"]],
                                        W, rank=2, bias=host(inp["bias"]))
-    G = il.iris_grid_size(Config(block_m=64, block_n=64))
+    G = il.iris_grid_size(Config(block_m=64, block_n=64), op=il.IRIS_OP_MM_RS)
     first = None
     for rows, cols, gw, mode in [(1, 8, 0, 0), (8, 64, 1, 0), (64, 200, G - 1, 0), (16, 24, 0, 1), (4, 200, 3, 0)]:
         note(f"mm_rs comm_block_m={rows} comm_block_n={cols} gemm_wgs={gw} mode={mode}")

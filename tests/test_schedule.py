@@ -4,7 +4,9 @@ The header is compiled into a small host program with hipcc (no GPU needed):
 for many grids it checks that the order is a bijection of [0, T) onto the
 tile grid, that tile_index inverts it, that the priority columns come first,
 and that the grouped order matches its definition (GROUP_M rows of tiles per
-group, column by column, rows fastest inside a group).
+group, column by column, rows fastest inside a group). The per-XCD queues
+must deal every position of the sequence to exactly one queue slot, each
+queue in increasing order, in blocks of Q dealt round-robin.
 """
 import os
 import shutil
@@ -46,7 +48,30 @@ int check(int n_pm, int n_pn, int gm, int lo, int hi) {
   }
   return 0;
 }
+int check_xcd(int T, int Q) {
+  std::vector<int> seen(T, 0);
+  for (int x = 0; x < kXcds; ++x) {
+    int prev = -1;
+    for (int j = 0;; ++j) {
+      const int t = xcd_tile(Q, x, j);
+      if (t >= T) break;
+      if (t <= prev) { printf("queue %d not increasing at j=%d\n", x, j); return 1; }
+      prev = t;
+      if ((t / Q) % kXcds != x) { printf("block of t=%d not dealt to %d\n", t, x); return 1; }
+      if (seen[t]++) { printf("t=%d twice\n", t); return 1; }
+      int x2, j2;
+      xcd_slot(Q, t, x2, j2);
+      if (x2 != x || j2 != j) { printf("xcd_slot(%d) wrong\n", t); return 1; }
+    }
+  }
+  for (int t = 0; t < T; ++t)
+    if (!seen[t]) { printf("t=%d never dealt\n", t); return 1; }
+  return 0;
+}
 int main() {
+  const int xs[][2] = {{1, 1}, {7, 1}, {256, 32}, {688, 32}, {1000, 7}, {32768, 32}, {100, 128}, {1024, 128}};
+  for (auto& s : xs)
+    if (check_xcd(s[0], s[1])) { printf("T=%d Q=%d\n", s[0], s[1]); return 1; }
   const int shapes[][5] = {{1, 1, 8, 0, 0},   {16, 16, 8, 0, 0},  {16, 43, 8, 0, 6},
                            {16, 43, 8, 37, 43}, {16, 43, 8, 5, 11}, {17, 5, 4, 0, 0},
                            {3, 7, 8, 2, 3},    {512, 64, 8, 0, 0}, {33, 9, 1, 0, 9},
