@@ -10,7 +10,11 @@ run. Prints ONE JSON line.
   value      GEMM TFLOP/s of the whole fused op: 2*M*N*K / (wall time per step)
   roofline   the fused persistent kernel against the dense fp16 MFMA peak:
              2*M*N*K / (average kernel duration from HIP events around each
-             launch on the op's stream)
+             launch on the op's stream). `traffic` is the kernel's HBM bytes
+             per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled by
+             what the same counters read for a plain device copy; it is read
+             from profiles/ and reported only while the kernel sources still
+             hash to the value recorded there (else null)
   comm       the communication units' HBM GB/s over their in-kernel window
   cpu_baseline  the CPU oracle on the full headline problem (gather + GEMM +
              bias in fp64) on the host's cores; also checks the GPU output
@@ -21,6 +25,7 @@ run. Prints ONE JSON line.
 Only one GPU is used: --gpus above 1 exits with a message.
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -32,6 +37,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+KERNEL_SOURCES = ("kernels.hip", "gemm_tile.hpp", "comm_units.hpp", "device_common.hpp", "schedule.hpp",
+                  "launch.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "persistent_kernel_ag_pow2_4k_traffic.txt")
 
 
 def parse():
@@ -43,6 +51,9 @@ def parse():
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--gemm-wgs", type=int, default=0,
+                    help="fixed gemm_wgs for the headline workload (no sweep)")
+    ap.add_argument("--kernel-hash", action="store_true", help="print the kernel source hash and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for HBM counter scaling)")
     return ap.parse_args()
@@ -98,31 +109,38 @@ class Case:
                                config=cfg)
 
     def sweep_candidates(self):
+        # the listed fractions {0.5, 0.75, 0.875} of the grid, plus splits that
+        # start most workgroups on the copy (1/8, 1/4) or on the GEMM (G-1);
+        # the library adds its static default
         G = self.G_wgs
-        fracs = [0.5, 0.75, 0.875]
+        fracs = [0.125, 0.25, 0.5, 0.75, 0.875]
         if self.w.op == "concurrent":
             fracs = [0.375, 0.5, 0.625, 0.75, 0.8125, 0.875, 0.9375]
-        return sorted({max(1, min(G - 1, int(math.floor(f * G)))) for f in fracs})
+        cands = {max(1, min(G - 1, int(math.floor(f * G)))) for f in fracs}
+        cands.add(G - 1)
+        return sorted(cands)
 
 
 def time_steps(case, cfg, steps, warmup):
-    """Wall time per step and the mean per-launch duration from HIP events."""
+    """Wall time per step (host clock, synchronized on both sides) and the mean
+    launch duration: HIP events on the op's stream (the stream the library
+    launches on) around the whole timed region, divided by the step count.
+    Steps are queued back to back, so the event span is the launches plus the
+    short gaps between them, with no per-launch event packets in between."""
     torch = case.torch
     for _ in range(warmup):
         case.step(cfg)
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
+    a.record(stream)
+    for _ in range(steps):
         case.step(cfg)
-        b.record(stream)
+    b.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    dur = sorted(a.elapsed_time(b) for a, b in ev)
-    return wall_ms, sum(dur) / len(dur), dur[len(dur) // 2]
+    return wall_ms, a.elapsed_time(b) / steps
 
 
 def windows(case):
@@ -132,25 +150,25 @@ def windows(case):
     return g, c
 
 
-def measure(name, steps, warmup, sweep):
+def measure(name, steps, warmup, sweep, fixed_wgs=0):
     il = __import__("gemm_collective_tile_amd")
     case = Case(name)
     w = case.w
     Config = il.Config
-    best = None
+    best = fixed_wgs or None
     sweep_ms = {}
-    if sweep:
+    if sweep and not fixed_wgs:
         cands = case.sweep_candidates()
         log(f"[{name}] sweeping gemm_wgs over {cands}")
         best, sweep_ms = il.iris_tune_gemm_wgs(case.op, cands, reps=5, **case.tune_kw)
     cfg = Config(gemm_wgs=best or 0)
     log(f"[{name}] timing fused mode, gemm_wgs={best}")
-    wall_ms, mean_ms, med_ms = time_steps(case, cfg, steps, warmup)
+    wall_ms, mean_ms = time_steps(case, cfg, steps, warmup)
     case.step(cfg)
     gwin, cwin = windows(case)
     log(f"[{name}] timing sequential mode")
     seq_cfg = Config(mode=il.IRIS_MODE_SEQUENTIAL)
-    seq_wall, seq_mean, _ = time_steps(case, seq_cfg, max(3, steps // 2), 2)
+    seq_wall, seq_mean = time_steps(case, seq_cfg, max(3, steps // 2), 2)
     case.step(seq_cfg)
     sgwin, scwin = windows(case)
     flops = w.gemm_flops
@@ -158,7 +176,7 @@ def measure(name, steps, warmup, sweep):
         "workload": name, "op": w.op, "M": w.M, "N": w.N, "K": w.K, "W": w.W,
         "gemm_wgs": best, "grid": case.G_wgs, "tile": "256x256x64",
         "sweep_ms": {str(k): round(v, 4) for k, v in sweep_ms.items()},
-        "fused_ms": round(wall_ms, 4), "kernel_ms": round(mean_ms, 4), "kernel_median_ms": round(med_ms, 4),
+        "fused_ms": round(wall_ms, 4), "kernel_ms": round(mean_ms, 4),
         "tflops": round(flops / (wall_ms * 1e-3) / 1e12, 2),
         "kernel_tflops": round(flops / (mean_ms * 1e-3) / 1e12, 2),
         "gemm_window_ms": round(gwin, 4) if gwin else None,
@@ -205,6 +223,30 @@ def cpu_baseline(case):
     }, bad, gathered_ok
 
 
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gemm_collective_tile_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per launch recorded in profiles/ for this kernel build, or None.
+    (Recorded at one gemm_wgs; the split moves work between queues but not the
+    bytes the launch moves.)"""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash() or kv.get("workload") != workload:
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
 def copy_calibration():
     import torch
     n = 1 << 29  # 1 GiB of fp16
@@ -222,6 +264,9 @@ def main():
         print(f"bench.py measures one GPU's share of the fused ops on a single MI355X; "
               f"--gpus {args.gpus} is not supported (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.kernel_hash:
+        print(kernel_source_hash())
+        return
     if args.copy_calibration:
         copy_calibration()
         return
@@ -229,7 +274,7 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(1)
-    head, case = measure(args.workload, args.steps, args.warmup, not args.no_sweep)
+    head, case = measure(args.workload, args.steps, args.warmup, not args.no_sweep, args.gemm_wgs)
     cpu = None
     if not args.no_cpu_baseline and case.w.op == "ag_mm" and case.w.gemm_flops <= 2 ** 38:
         cpu, bad, gathered_ok = cpu_baseline(case)
@@ -270,8 +315,9 @@ def main():
         },
         "roofline": {
             "bound": "mfma", "achieved": w["kernel_tflops"], "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
-            "frac": w["mfma_frac"], "traffic": None,
-            "kernel": f"persistent_kernel (fused {w['op']}), mean of {args.steps} launches: {w['kernel_ms']} ms",
+            "frac": w["mfma_frac"], "traffic": recorded_traffic(w["workload"]),
+            "kernel": f"persistent_kernel<1,256,256> (fused {w['op']}), HIP-event mean over {args.steps} "
+                      f"back-to-back launches: {w['kernel_ms']} ms",
         },
         "comm": {
             "gbps": w["comm_gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": w.get("comm_hbm_frac"),
