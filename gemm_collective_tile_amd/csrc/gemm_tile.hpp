@@ -15,14 +15,21 @@
 //   * v_mfma_f32_32x32x16_f16 computes 32x32 output blocks, K step 16. Lane
 //     l supplies, for its row (A) or column (B) l % 32, the 8 consecutive k
 //     8*(l/32) .. 8*(l/32)+7 of the 16-wide k slice.
-//   * Operands go global -> LDS with buffer_load ... lds (LDS DMA): no
-//     registers, no LDS write instructions. One wave instruction moves
-//     1 KiB: lane l's 16 bytes land at LDS base + 16 l, so the layout in LDS
-//     is chosen by which global 16-byte chunk each lane fetches.
-//   * K is walked in steps of BK = 32 through a ring of NSTAGE = 4 LDS
-//     stages: A as [BM][32] (64-byte rows), B as [32][BN] (row-major, as
-//     stored). The 16-byte chunks of every row are XOR-swizzled by a
-//     function of the row so that the fragment reads spread over the banks.
+//   * K is walked in steps of BK = 64. Each thread loads its share of a
+//     step's A and B tiles (16-byte buffer loads, default caching) into
+//     registers two steps ahead and writes them to one of two LDS stages
+//     one step ahead: A as
+//     [BM][64] (128-byte rows: every load request fills a whole 128-byte
+//     line; at 64-byte rows each line was fetched twice, and the operand
+//     stream from L2 is bounded by the misses a CU keeps in flight), B as
+//     [64][BN] (row-major, as stored). The 16-byte chunks of every row are
+//     XOR-swizzled by a function of the row so that the fragment reads and
+//     the LDS writes spread over the banks.
+//     Loads go through registers rather than straight into LDS (the
+//     buffer_load ... lds form): on gfx950 an ordinary LDS read waits for
+//     every LDS-targeted load its wave still has in flight, whatever the
+//     addresses, so with a load ring in flight each A fragment read would
+//     wait out a global-memory latency.
 //   * A fragments: one ds_read_b128 (8 consecutive k of one row).
 //     B fragments: two ds_read_b64_tr_b16. In each 16-lane group that
 //     instruction returns to lane j element (j & 3) of the 8-byte chunks
@@ -34,11 +41,14 @@
 //   * Masking of ragged edges: buffer loads whose offset is past the
 //     resource size return zeros (M and K rows), and chunks past N or past
 //     K inside a row are given an out-of-range offset.
-//   * Pipeline: loads run NSTAGE - 1 steps ahead. Each K step issues the
-//     loads of step t+3 and the fragment reads of slice 1 under the MFMAs of
-//     slice 0; halfway through slice 1 it waits for its own loads of step
-//     t+1, passes the one barrier of the step, and reads the slice-0
-//     fragments of step t+1 under the rest of slice 1.
+//   * Pipeline of step t (stage t % 2 holds it, 4 k slices of 16): the
+//     loads of step t+2 go out one every few MFMAs over the whole step (a
+//     burst of them fills the address queue of the CU's memory pipeline and
+//     stalls the wave with the MFMA pipe empty); the fragment reads of slice
+//     s+1 run under the MFMAs of slice s; the registers of step t+1 (loaded
+//     during step t-1) are written to the other stage, spread over the part
+//     before the barrier; one barrier; the slice-0 fragments of step t+1 are
+//     read under the second half of the last slice.
 //   * The MFMA takes B as its first operand and A as its second, so each
 //     lane ends up holding 4 consecutive output columns of one row: the
 //     epilogue stores 8 bytes per lane after adding the bias.
@@ -49,15 +59,16 @@
 namespace iris {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 template <int BM_, int BN_>
 struct TileShape {
-  static constexpr int BM = BM_, BN = BN_, BK = 32, NSTAGE = 4;
+  static constexpr int BM = BM_, BN = BN_, BK = 64, NSTAGE = 2;
+  static constexpr int NSL = BK / 16;                 // k slices (MFMA K steps) per K step
   static constexpr int WTM = BM / 2, WTN = BN / 2;    // per-wave sub-tile
   static constexpr int FM = WTM / 32, FN = WTN / 32;  // 32x32 blocks per wave
-  static constexpr int RA = BK * 2;                   // bytes per A row in LDS (64)
+  static constexpr int RA = BK * 2;                   // bytes per A row in LDS (128)
+  static constexpr int CPR_A = BK / 8;                // 16-byte chunks per A row
   static constexpr int RB = BN * 2;                   // bytes per B row in LDS
   static constexpr int CPR_B = BN / 8;                // 16-byte chunks per B row
   static constexpr int A_STAGE = BM * RA;
@@ -65,31 +76,21 @@ struct TileShape {
   static constexpr int STAGE = A_STAGE + B_STAGE;
   static constexpr int B_RING = NSTAGE * A_STAGE;     // LDS: [A stages | B stages]
   static constexpr int LDS_BYTES = NSTAGE * STAGE;
-  static constexpr int A_DMA = A_STAGE / 1024 / 4;    // 1 KiB DMA instructions per wave per step
-  static constexpr int B_DMA = B_STAGE / 1024 / 4;
-  static constexpr int RPB = 1024 / RB;               // B rows per DMA instruction
+  static constexpr int A_LD = A_STAGE / 16 / 256;     // 16-byte chunks per thread per step
+  static constexpr int B_LD = B_STAGE / 16 / 256;
   static_assert(FM >= 1 && FN >= 1, "tile too small for 32x32 blocks");
-  static_assert(A_DMA >= 1 && B_DMA >= 1, "tile too small for 4 waves of 1 KiB loads");
+  static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for 256 threads of 16-byte loads");
 };
 
-// swizzle of the 16-byte chunks of a 64-byte A row (4 chunks)
-#ifndef IRIS_SWZ_A
-#define IRIS_SWZ_A 1
-#endif
-__device__ __forceinline__ uint32_t swz_a(uint32_t r) {
-  if (IRIS_SWZ_A == 1) return (r >> 2) & 3u;
-  if (IRIS_SWZ_A == 2) return r & 3u;
-  if (IRIS_SWZ_A == 3) return 0u;
-  if (IRIS_SWZ_A == 4) return ((r >> 1) ^ (r >> 2)) & 3u;
-  return ((r >> 1) ^ (r >> 3)) & 3u;
-}
+// swizzle of the 16-byte chunks of a 128-byte A row (8 chunks): 16
+// consecutive rows reading the same logical chunk land on 16 different
+// 16-byte bank groups (row parity picks the half of the 256-byte bank
+// cycle, (r >> 1) & 7 the slot in it)
+__device__ __forceinline__ uint32_t swz_a(uint32_t r) { return (r >> 1) & 7u; }
 // swizzle of the 16-byte chunks of a B row, by k row
-#ifndef IRIS_SWZ_B_MUL
-#define IRIS_SWZ_B_MUL 4
-#endif
 template <class S>
 __device__ __forceinline__ uint32_t swz_b(uint32_t k) {
-  return ((k & 3u) * IRIS_SWZ_B_MUL) & (uint32_t)(S::CPR_B - 1);
+  return ((k & 3u) * 4u) & (uint32_t)(S::CPR_B - 1);
 }
 
 struct GemmArgs {
@@ -106,43 +107,46 @@ struct GemmArgs {
 
 template <class S>
 struct GemmPipe {
-  // per-lane byte offsets of the DMA chunks within a K step's resource
-  uint32_t a_off[S::A_DMA];
-  uint32_t a_kc;             // k offset (elements) of this lane's A chunks
-  uint32_t b_off[S::B_DMA];
+  static constexpr int NLD = S::A_LD + S::B_LD;
+  // per-thread byte offsets of the loaded chunks within a K step's resource,
+  // and where they go in an LDS stage
+  uint32_t a_off[S::A_LD];
+  uint32_t a_kc;             // k offset (elements) of this thread's A chunks
+  uint32_t b_off[S::B_LD];
+  uint32_t a_lds[S::A_LD];
+  uint32_t b_lds[S::B_LD];   // includes B_RING
   // LDS byte offsets of the fragment reads within the A / B rings
-  uint32_t ra_base[2];        // A, per k slice
+  uint32_t ra_base[S::NSL];   // A, per k slice
   uint32_t rb_base[S::FN];    // B, per 32-column block (includes B_RING)
-  uint32_t wave;              // wave index, uniform (scalar)
 
   __device__ __forceinline__ void setup(const GemmArgs& g, int n0) {
-    const uint32_t l = threadIdx.x & 63;
-    const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t tid = threadIdx.x;
+    const uint32_t l = tid & 63;
+    const uint32_t w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t wm = w >> 1, wn = w & 1;
-    wave = w;
-    // A instruction b covers tile rows 16 b .. 16 b + 15: lane l takes row
-    // 16 b + (l >> 2) and LDS chunk l & 3, i.e. logical chunk (l & 3) ^ swz
-    // (swz_a(16 b + r) == swz_a(r), so the chunk is the same for every b)
-    const uint32_t ca = (l & 3) ^ swz_a(l >> 2);
+    // A chunk c = tid + 256 n: row c / 8, k chunk c % 8 (= tid % 8 for every n)
+    const uint32_t ca = tid & (S::CPR_A - 1);
     a_kc = 8 * ca;
 #pragma unroll
-    for (int n = 0; n < S::A_DMA; ++n) {
-      const uint32_t r = 16 * (w * S::A_DMA + n) + (l >> 2);
+    for (int n = 0; n < S::A_LD; ++n) {
+      const uint32_t r = (tid + 256 * n) / S::CPR_A;
       a_off[n] = (uint32_t)((r * g.lda + 8 * ca) * 2);
+      a_lds[n] = r * S::RA + ((ca ^ swz_a(r)) << 4);
     }
+    // B chunk c = tid + 256 n: k row c / CPR_B, column chunk c % CPR_B
 #pragma unroll
-    for (int n = 0; n < S::B_DMA; ++n) {
-      // B instruction b covers k rows RPB b .. RPB b + RPB - 1
-      const uint32_t k = S::RPB * (w * S::B_DMA + n) + l / S::CPR_B;
-      const uint32_t c = (l % S::CPR_B) ^ swz_b<S>(k);
-      const bool ok = n0 + 8 * (int)c < g.N;
-      b_off[n] = ok ? (uint32_t)((k * g.ldb + 8 * c) * 2) : kOob;
+    for (int n = 0; n < S::B_LD; ++n) {
+      const uint32_t c = tid + 256 * n;
+      const uint32_t k = c / S::CPR_B, ch = c % S::CPR_B;
+      const bool ok = n0 + 8 * (int)ch < g.N;
+      b_off[n] = ok ? (uint32_t)((k * g.ldb + 8 * ch) * 2) : kOob;
+      b_lds[n] = S::B_RING + k * S::RB + ((ch ^ swz_b<S>(k)) << 4);
     }
     {
       const uint32_t r = wm * S::WTM + (l & 31);
       const uint32_t h = l >> 5;
 #pragma unroll
-      for (int sl = 0; sl < 2; ++sl) ra_base[sl] = r * S::RA + (((2 * sl + h) ^ swz_a(r)) << 4);
+      for (int sl = 0; sl < S::NSL; ++sl) ra_base[sl] = r * S::RA + (((2 * sl + h) ^ swz_a(r)) << 4);
     }
     {
       const uint32_t grp = l >> 4, e = (l >> 2) & 3, q = l & 3;
@@ -158,7 +162,7 @@ struct GemmPipe {
   // Buffer resources of K step `step` (k0 = step * BK): rows past M and K
   // fall outside them.
   struct Rsrc {
-    u32x4 a, b;
+    __amdgpu_buffer_rsrc_t a, b;
     bool kok;
   };
   __device__ __forceinline__ Rsrc rsrc(const GemmArgs& g, int m0, int n0, int step) const {
@@ -166,23 +170,34 @@ struct GemmPipe {
     const int k0 = step * S::BK;
     const int rows = min(S::BM, g.M - m0);
     const int64_t abytes = (int64_t)rows * g.lda * 2 - (int64_t)k0 * 2;
-    r.a = rsrc_words(g.A + (int64_t)m0 * g.lda + k0, abytes > 0 ? (uint32_t)abytes : 0u);
+    r.a = make_rsrc(g.A + (int64_t)m0 * g.lda + k0, abytes > 0 ? (uint32_t)abytes : 0u);
     const int krows = min(S::BK, g.K - k0);
-    r.b = rsrc_words(g.B + (int64_t)k0 * g.ldb + n0,
-                     krows > 0 ? (uint32_t)((int64_t)krows * g.ldb * 2 - (int64_t)n0 * 2) : 0u);
+    r.b = make_rsrc(g.B + (int64_t)k0 * g.ldb + n0,
+                    krows > 0 ? (uint32_t)((int64_t)krows * g.ldb * 2 - (int64_t)n0 * 2) : 0u);
     r.kok = k0 + (int)a_kc < g.K;
     return r;
   }
 
-  // DMA number D (A instructions first, then B) of a K step into ring slot ST
+  // a K step's share of this thread, in registers
+  struct Regs {
+    u32x4 v[NLD];
+  };
+
+  // load item D (A chunks first, then B) of a K step
   template <int D>
-  __device__ __forceinline__ void dma(const Rsrc& r, uint32_t lds_base, int ST) const {
-    if constexpr (D < S::A_DMA) {
-      dma16(r.a, lds_base + ST * S::A_STAGE + (wave * S::A_DMA + D) * 1024, r.kok ? a_off[D] : kOob);
-    } else {
-      constexpr int n = D - S::A_DMA;
-      dma16(r.b, lds_base + S::B_RING + ST * S::B_STAGE + (wave * S::B_DMA + n) * 1024, b_off[n]);
-    }
+  __device__ __forceinline__ void load(const Rsrc& r, Regs& R) const {
+    if constexpr (D < S::A_LD)
+      R.v[D] = buf_load16(r.a, r.kok ? a_off[D] : kOob);
+    else
+      R.v[D] = buf_load16(r.b, b_off[D - S::A_LD]);
+  }
+  // write item D to LDS stage ST
+  template <int D>
+  __device__ __forceinline__ void store(char* lds, int ST, const Regs& R) const {
+    if constexpr (D < S::A_LD)
+      *(u32x4*)(lds + ST * S::A_STAGE + a_lds[D]) = R.v[D];
+    else
+      *(u32x4*)(lds + ST * S::B_STAGE + b_lds[D - S::A_LD]) = R.v[D];
   }
 
   struct Frags {
@@ -190,8 +205,8 @@ struct GemmPipe {
     f16x8 b[S::FN];
   };
 
-  // fragment read item X of k slice SL from ring slot ST: items alternate
-  // a0, b0, a1, b1, ... so that the operands of the first MFMA blocks arrive
+  // fragment read item X of k slice SL from stage ST: items alternate a0,
+  // b0, a1, b1, ... so that the operands of the first MFMA blocks arrive
   // first
   template <int SL, int X>
   __device__ __forceinline__ void read(const char* lds, int ST, Frags& f) const {
@@ -221,60 +236,10 @@ __device__ __forceinline__ void mma_block(f32x16 (&acc)[S::FM][S::FN], const typ
   acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
-// s_waitcnt with the vector-memory counter limited to VM and the LDS counter
-// to LG (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-template <int VM, int LG = 15>
-__device__ __forceinline__ void wait_cnt() {
-  static_assert(VM >= 0 && VM < 64 && LG >= 0 && LG < 16, "counter range");
-  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LG << 8));
-}
-
-// Slots of a K step, issued in program order:
-//   region 1: slot k = MFMA block k of slice 0 (fragments f0), then fragment
-//             read item k of slice 1 into f1, then DMA k of step t+3 (the
-//             DMAs go first so they have the most time to land); then the first half of slice 1's MFMA blocks.
-//   wait for this wave's DMAs of step t+1 and its own LDS reads; barrier.
-//   region 2: the second half of slice 1's blocks, each followed by two
-//             fragment reads of slice 0 of step t+1 (stage NXT) into f0.
-template <class S, int K, int NM, int NR, int ND>
-__device__ __forceinline__ void region1(const GemmPipe<S>& P, const typename GemmPipe<S>::Rsrc& r,
-                                        const char* lds, uint32_t lds_base, int cur, int ahead,
-                                        typename GemmPipe<S>::Frags& f0, typename GemmPipe<S>::Frags& f1,
-                                        f32x16 (&acc)[S::FM][S::FN]) {
-  constexpr int SLOTS = NM > NR ? (NM > ND ? NM : ND) : (NR > ND ? NR : ND);
-  if constexpr (K < SLOTS) {
-    if constexpr (K < NM) mma_block<S, K>(acc, f0);
-    if constexpr (K < NR) P.template read<1, K>(lds, cur, f1);
-    constexpr int D = K;
-    if constexpr (D >= 0 && D < ND) P.template dma<D>(r, lds_base, ahead);
-    region1<S, K + 1, NM, NR, ND>(P, r, lds, lds_base, cur, ahead, f0, f1, acc);
-  }
-}
-
-template <class S, int K, int K1, int NM>
-__device__ __forceinline__ void mma_range(f32x16 (&acc)[S::FM][S::FN], const typename GemmPipe<S>::Frags& f) {
-  if constexpr (K < K1 && K < NM) {
-    mma_block<S, K>(acc, f);
-    mma_range<S, K + 1, K1, NM>(acc, f);
-  }
-}
-
-template <class S, int K, int NM, int NR, int X>
-__device__ __forceinline__ void region2(const GemmPipe<S>& P, const char* lds, int nxt,
-                                        typename GemmPipe<S>::Frags& f0, const typename GemmPipe<S>::Frags& f1,
-                                        f32x16 (&acc)[S::FM][S::FN]) {
-  if constexpr (K < NM || X < NR) {
-    if constexpr (K < NM) mma_block<S, K>(acc, f1);
-    if constexpr (X < NR) P.template read<0, X>(lds, nxt, f0);
-    if constexpr (X + 1 < NR) P.template read<0, X + 1>(lds, nxt, f0);
-    region2<S, K + 1, NM, NR, X + 2>(P, lds, nxt, f0, f1, acc);
-  }
-}
-
 // Scheduling groups (masks of __builtin_amdgcn_sched_group_barrier: 0x8
-// MFMA, 0x100 LDS read). Region 1: slot k = one MFMA, then the LDS reads of
-// fragment item k (1 for an A item, 2 for a B item). Region 2: one MFMA, then
-// the reads of two items. The DMA (inline asm) keeps its program order.
+// MFMA, 0x20 global load, 0x100 LDS read, 0x200 LDS write). Every slot pins
+// one MFMA, then the LDS reads of its fragment items (1 for an A item, 2 for
+// a B item), then its load and its LDS write, if any.
 template <class S>
 __device__ constexpr int item_reads(int x) {
   constexpr int NMIN = S::FM < S::FN ? S::FM : S::FN;
@@ -283,61 +248,153 @@ __device__ constexpr int item_reads(int x) {
   return is_a ? 1 : 2;
 }
 
-template <class S, int K, int NM>
-__device__ __forceinline__ void sched_region1() {
-  if constexpr (K < NM) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if constexpr (item_reads<S>(K) > 0) __builtin_amdgcn_sched_group_barrier(0x100, item_reads<S>(K), 0);
-    sched_region1<S, K + 1, NM>();
+template <int MFMA, int READS, int LOADS, int WRITES>
+__device__ __forceinline__ void pin_slot() {
+  if constexpr (MFMA > 0) __builtin_amdgcn_sched_group_barrier(0x008, MFMA, 0);
+  if constexpr (READS > 0) __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+  if constexpr (LOADS > 0) __builtin_amdgcn_sched_group_barrier(0x020, LOADS, 0);
+  if constexpr (WRITES > 0) __builtin_amdgcn_sched_group_barrier(0x200, WRITES, 0);
+}
+
+// Slot plan of a K step with NM MFMA blocks per k slice and NSL slices.
+// Slice s owns slots s SPAN .. s SPAN + SPAN - 1, SPAN = max(NM, NR): slot
+// s SPAN + b runs block b of slice s (b < NM) and reads fragment item b of
+// slice s+1 (b < NR), so every read of a slice precedes its first block.
+// Region 1 (before the barrier) ends after the first NM/2 blocks of the last
+// slice (NSLOT slots); region 2 holds the rest of that slice (slots NSLOT ..
+// NSL SPAN - 1) with the slice-0 reads of step t+1. The NLD loads of step
+// t+2 go every LSP slots over the whole step, the LDS writes of step t+1
+// every WSP slots over region 1. Region 1 grows extra slots without an MFMA
+// when a small tile has more items than slots.
+template <class S>
+struct Plan {
+  static constexpr int NM = S::FM * S::FN, NR = S::FM + S::FN, NLD = S::A_LD + S::B_LD;
+  static constexpr int NSL = S::NSL;
+  static constexpr int max2(int a, int b) { return a > b ? a : b; }
+  static constexpr int SPAN = max2(NM, NR);
+  static constexpr int NSLOT = (NSL - 1) * SPAN + NM / 2;
+  static constexpr int NSTEP = NSL * SPAN;  // slots of the whole step
+  static constexpr int LSP = NSTEP / NLD > 0 ? NSTEP / NLD : 1;
+  static constexpr int WSP = NSLOT / NLD > 0 ? NSLOT / NLD : 1;
+  static constexpr int W_END = WSP * (NLD - 1) + 1;
+  static constexpr int READ_END = (NSL - 2) * SPAN + NR;
+  static constexpr int REGION1 = max2(max2(NSLOT, READ_END), W_END);
+  static constexpr bool is_mfma(int k) { return k < NSLOT && k % SPAN < NM; }
+  static constexpr bool is_load(int k) { return k % LSP == 0 && k / LSP < NLD; }
+  static constexpr int load_item(int k) { return k / LSP; }
+  static constexpr bool is_write(int k) { return k % WSP == 0 && k / WSP < NLD; }
+  static constexpr int write_item(int k) { return k / WSP; }
+  static constexpr bool is_read(int k) { return k < (NSL - 1) * SPAN && k % SPAN < NR; }
+  static constexpr int read_slice(int k) { return k / SPAN + 1; }
+  static constexpr int read_item(int k) { return k % SPAN; }
+  // loads that do not fit in the slots of the step (a small tile) go after
+  // region 2
+  static constexpr int LOADS_IN_STEP = NSTEP / LSP < NLD ? NSTEP / LSP : NLD;
+};
+
+// fragments of slice s live in f[s % 2]
+template <class S, int SL>
+__device__ __forceinline__ typename GemmPipe<S>::Frags& frag(typename GemmPipe<S>::Frags& f0,
+                                                            typename GemmPipe<S>::Frags& f1) {
+  if constexpr (SL % 2 == 0)
+    return f0;
+  else
+    return f1;
+}
+
+template <class S, int K>
+__device__ __forceinline__ void region1(const GemmPipe<S>& P, const typename GemmPipe<S>::Rsrc& r, char* lds,
+                                        int cur, int nxt, typename GemmPipe<S>::Regs& ahead,
+                                        const typename GemmPipe<S>::Regs& next, typename GemmPipe<S>::Frags& f0,
+                                        typename GemmPipe<S>::Frags& f1, f32x16 (&acc)[S::FM][S::FN]) {
+  using PL = Plan<S>;
+  if constexpr (K < PL::REGION1) {
+    if constexpr (PL::is_mfma(K)) mma_block<S, K % PL::SPAN>(acc, frag<S, K / PL::SPAN>(f0, f1));
+    constexpr bool RD = PL::is_read(K);
+    if constexpr (RD)
+      P.template read<PL::read_slice(K), PL::read_item(K)>(lds, cur, frag<S, PL::read_slice(K)>(f0, f1));
+    constexpr bool LD = PL::is_load(K) && PL::load_item(K) < PL::LOADS_IN_STEP;
+    if constexpr (LD) P.template load<PL::load_item(K)>(r, ahead);
+    if constexpr (PL::is_write(K)) P.template store<PL::write_item(K)>(lds, nxt, next);
+    pin_slot<PL::is_mfma(K) ? 1 : 0, RD ? item_reads<S>(PL::read_item(K)) : 0, LD ? 1 : 0,
+             PL::is_write(K) ? 1 : 0>();
+    region1<S, K + 1>(P, r, lds, cur, nxt, ahead, next, f0, f1, acc);
   }
 }
 
-template <class S, int K, int NM, int X>
-__device__ __forceinline__ void sched_region2() {
-  if constexpr (K < NM) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    constexpr int R = item_reads<S>(X) + item_reads<S>(X + 1);
-    if constexpr (R > 0) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
-    sched_region2<S, K + 1, NM, X + 2>();
+// Region 2 (after the barrier): the second half of the last slice's blocks,
+// each followed by two fragment reads of slice 0 of step t+1 (stage NXT);
+// slot K (numbered as in the whole step) also carries its load, if any.
+template <class S, int K, int X>
+__device__ __forceinline__ void region2(const GemmPipe<S>& P, const typename GemmPipe<S>::Rsrc& r,
+                                        const char* lds, int nxt, typename GemmPipe<S>::Regs& ahead,
+                                        typename GemmPipe<S>::Frags& f0, typename GemmPipe<S>::Frags& f1,
+                                        f32x16 (&acc)[S::FM][S::FN]) {
+  using PL = Plan<S>;
+  constexpr int B = K - PL::NSLOT + PL::NM / 2;  // block of the last slice
+  if constexpr (B < PL::NM || X < PL::NR) {
+    if constexpr (B < PL::NM) mma_block<S, B>(acc, frag<S, PL::NSL - 1>(f0, f1));
+    if constexpr (X < PL::NR) P.template read<0, X>(lds, nxt, f0);
+    if constexpr (X + 1 < PL::NR) P.template read<0, X + 1>(lds, nxt, f0);
+    constexpr bool LD = PL::is_load(K) && PL::load_item(K) < PL::LOADS_IN_STEP;
+    if constexpr (LD) P.template load<PL::load_item(K)>(r, ahead);
+    pin_slot<B < PL::NM ? 1 : 0, item_reads<S>(X) + item_reads<S>(X + 1), LD ? 1 : 0, 0>();
+    region2<S, K + 1, X + 2>(P, r, lds, nxt, ahead, f0, f1, acc);
   }
 }
 
-// One K step on ring slot ST (compile-time), fragments of slice 0 already
-// in f0. Loads step t+3 into slot (ST+3) % NSTAGE.
+template <class S, int D>
+__device__ __forceinline__ void load_rest(const GemmPipe<S>& P, const typename GemmPipe<S>::Rsrc& r,
+                                          typename GemmPipe<S>::Regs& R) {
+  if constexpr (D < GemmPipe<S>::NLD) {
+    P.template load<D>(r, R);
+    load_rest<S, D + 1>(P, r, R);
+  }
+}
+
+// One K step t on LDS stage ST = t % 2, fragments of slice 0 already in f0.
+// `next` holds step t+1 (loaded during step t-1) and is written to the other
+// stage, which was last read before the previous step's barrier; `ahead`
+// (written to LDS during step t-1) receives step t+2.
 template <class S, int ST>
-__device__ __forceinline__ void k_step(const GemmPipe<S>& P, const GemmArgs& g, int m0, int n0, int t,
-                                       const char* lds, uint32_t lds_base, typename GemmPipe<S>::Frags& f0,
-                                       typename GemmPipe<S>::Frags& f1, f32x16 (&acc)[S::FM][S::FN]) {
-  constexpr int NS = S::NSTAGE;
-  constexpr int CUR = ST % NS, NXT = (ST + 1) % NS, AHEAD = (ST + NS - 1) % NS;
-  constexpr int NM = S::FM * S::FN, NR = S::FM + S::FN, ND = S::A_DMA + S::B_DMA;
-  constexpr int H1 = NM / 2;
+__device__ __forceinline__ void k_step(const GemmPipe<S>& P, const GemmArgs& g, int m0, int n0, int t, char* lds,
+                                       typename GemmPipe<S>::Regs& ahead, const typename GemmPipe<S>::Regs& next,
+                                       typename GemmPipe<S>::Frags& f0, typename GemmPipe<S>::Frags& f1,
+                                       f32x16 (&acc)[S::FM][S::FN]) {
+  static_assert(S::NSL % 2 == 0, "slice 0 of the next step reuses f0");
+  using PL = Plan<S>;
+  constexpr int CUR = ST, NXT = ST ^ 1;
   // keep the scheduler from hoisting this step's reads into the previous
   // step (that would hold three fragment sets live and spill)
   __builtin_amdgcn_sched_barrier(0);
-  const typename GemmPipe<S>::Rsrc r = P.rsrc(g, m0, n0, t + NS - 1);
-  region1<S, 0, NM, NR, ND>(P, r, lds, lds_base, CUR, AHEAD, f0, f1, acc);
-  mma_range<S, 0, H1, NM>(acc, f1);
-  sched_region1<S, 0, NM + H1>();
-  // step t+1 complete for this wave (t+2 and t+3 may be in flight), and
-  // every fragment read of this slot done, before the barrier. The barrier
-  // must carry the workgroup fences: without them the compiler may hoist the
-  // next step's LDS reads above it.
+  const typename GemmPipe<S>::Rsrc r = P.rsrc(g, m0, n0, t + 2);
+  region1<S, 0>(P, r, lds, CUR, NXT, ahead, next, f0, f1, acc);
+  // every wave's LDS writes of step t+1 and reads of stage CUR are done at
+  // the barrier (it carries the workgroup fence, which also keeps the
+  // compiler from hoisting the next reads above it)
   __builtin_amdgcn_sched_barrier(0);
-  wait_cnt<(NS - 2) * ND, 0>();
   __syncthreads();
   __builtin_amdgcn_sched_barrier(0);
-  region2<S, H1, NM, NR, 0>(P, lds, NXT, f0, f1, acc);
-  sched_region2<S, H1, NM, 0>();
+  region2<S, PL::NSLOT, 0>(P, r, lds, NXT, ahead, f0, f1, acc);
+  if constexpr (PL::LOADS_IN_STEP < PL::NLD) load_rest<S, PL::LOADS_IN_STEP>(P, r, ahead);
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <class S, int D, int ND>
-__device__ __forceinline__ void dma_all(const GemmPipe<S>& P, const typename GemmPipe<S>::Rsrc& r,
-                                        uint32_t lds_base, int slot) {
-  if constexpr (D < ND) {
-    P.template dma<D>(r, lds_base, slot);
-    dma_all<S, D + 1, ND>(P, r, lds_base, slot);
+template <class S, int D>
+__device__ __forceinline__ void load_all(const GemmPipe<S>& P, const typename GemmPipe<S>::Rsrc& r,
+                                         typename GemmPipe<S>::Regs& R) {
+  if constexpr (D < GemmPipe<S>::NLD) {
+    P.template load<D>(r, R);
+    load_all<S, D + 1>(P, r, R);
+  }
+}
+
+template <class S, int D>
+__device__ __forceinline__ void store_all(const GemmPipe<S>& P, char* lds, int ST,
+                                          const typename GemmPipe<S>::Regs& R) {
+  if constexpr (D < GemmPipe<S>::NLD) {
+    P.template store<D>(lds, ST, R);
+    store_all<S, D + 1>(P, lds, ST, R);
   }
 }
 
@@ -351,13 +408,12 @@ __device__ __forceinline__ void read_all(const GemmPipe<S>& P, const char* lds, 
 }
 
 // Computes the tile at (m0, n0) and writes it to C. `lds` must hold
-// S::LDS_BYTES. Starts and ends with a workgroup barrier so callers may
-// reuse the LDS around it.
+// S::LDS_BYTES. Starts with a workgroup barrier so callers may reuse the LDS
+// before it; the LDS writes of its last step target a stage nobody reads,
+// and the caller's next use of the LDS starts with a barrier.
 template <class S>
 __device__ void gemm_tile(const GemmArgs& g, int m0, int n0, char* lds) {
   using P_t = GemmPipe<S>;
-  constexpr int NS = S::NSTAGE;
-  constexpr int ND = S::A_DMA + S::B_DMA;  // DMA instructions per wave per step
   constexpr int NR = S::FM + S::FN;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -375,33 +431,25 @@ __device__ void gemm_tile(const GemmArgs& g, int m0, int n0, char* lds) {
   P_t P;
   P.setup(g, n0);
   typename P_t::Frags f0, f1;
-  // LDS byte address of the stage ring, for the DMA
-  const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)lds);
+  typename P_t::Regs R0, R1;
 
+  load_all<S, 0>(P, P.rsrc(g, m0, n0, 0), R0);
+  load_all<S, 0>(P, P.rsrc(g, m0, n0, 1), R1);
   __syncthreads();  // previous users of the LDS are done
-  dma_all<S, 0, ND>(P, P.rsrc(g, m0, n0, 0), lds_base, 0);
-  dma_all<S, 0, ND>(P, P.rsrc(g, m0, n0, 1), lds_base, 1);
-  dma_all<S, 0, ND>(P, P.rsrc(g, m0, n0, 2), lds_base, 2);
-  wait_cnt<(NS - 2) * ND>();  // this wave's part of step 0 has landed
+  store_all<S, 0>(P, lds, 0, R0);
   __syncthreads();
   read_all<S, 0, NR>(P, lds, 0, f0);
 
-  // The ring has NS = 4 slots: unroll by 4 so every slot offset is a
-  // constant. The step count is rounded up to a multiple of 4 (a loop with one
-  // exit keeps the accumulators in place); the extra steps read only
-  // out-of-range zeros and add exact zeros to accumulators that start at +0,
-  // so they change no bit of the result.
-  static_assert(NS == 4, "the K loop is unrolled by the ring size");
-  const int nk4 = (nk + 3) & ~3;
-  for (int t = 0; t < nk4; t += 4) {
-    k_step<S, 0>(P, g, m0, n0, t, lds, lds_base, f0, f1, acc);
-    k_step<S, 1>(P, g, m0, n0, t + 1, lds, lds_base, f0, f1, acc);
-    k_step<S, 2>(P, g, m0, n0, t + 2, lds, lds_base, f0, f1, acc);
-    k_step<S, 3>(P, g, m0, n0, t + 3, lds, lds_base, f0, f1, acc);
+  // Two stages and two register sets: unroll by 2 so both are named at
+  // compile time. The step count is rounded up to even (a loop with one
+  // exit keeps the accumulators in place); the extra step reads only
+  // out-of-range zeros and adds exact zeros to accumulators that start at
+  // +0, so it changes no bit of the result.
+  const int nk2 = (nk + 1) & ~1;
+  for (int t = 0; t < nk2; t += 2) {
+    k_step<S, 0>(P, g, m0, n0, t, lds, R0, R1, f0, f1, acc);
+    k_step<S, 1>(P, g, m0, n0, t + 1, lds, R1, R0, f0, f1, acc);
   }
-  // loads issued past the last step target stages no one reads; let them
-  // land before the LDS is reused
-  wait_cnt<0, 0>();
 
   // epilogue: lane holds row m = lane & 31 of each 32x32 block and, for
   // q = 0..3, columns 8q + 4*(lane >> 5) + 0..3.
