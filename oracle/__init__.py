@@ -58,6 +58,13 @@ def _load():
     lib.oracle_matmul_all_reduce.argtypes = [
         _u16p, _u16p, _u16p, ctypes.c_int, ctypes.POINTER(_u16p), ctypes.c_int,
         _i64, _i64, _i64, _i64, _i64, _f64p, ctypes.c_int]
+    lib.oracle_matmul_all_gather.argtypes = [
+        _u16p, _u16p, _u16p, ctypes.c_int, ctypes.POINTER(_u16p), ctypes.c_int, ctypes.c_int,
+        _i64, _i64, _i64, _i64, _i64, _f64p, ctypes.c_int]
+    lib.oracle_all_gather_flat.argtypes = [ctypes.POINTER(_u16p), ctypes.c_int, _i64, _u16p]
+    lib.oracle_reduce_scatter_flat.argtypes = [ctypes.POINTER(_u16p), ctypes.c_int, _i64, ctypes.c_int, _f64p]
+    lib.oracle_all_to_all_flat.argtypes = [ctypes.POINTER(_u16p), ctypes.c_int, _i64, ctypes.c_int, _u16p]
+    lib.oracle_broadcast_flat.argtypes = [ctypes.POINTER(_u16p), ctypes.c_int, _i64, ctypes.c_int, _u16p]
     lib.oracle_default_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -201,3 +208,60 @@ def matmul_all_reduce(A, B, partials, W, bias=None, bias_along_m=False, rows=Non
 def all_reduce(bufs) -> np.ndarray:
     """Elementwise sum of W fp16 buffers (the all_reduce beside an independent GEMM)."""
     return sum_buffers(bufs)
+
+
+def matmul_all_gather(A, B, peers, W, rank=0, bias=None, bias_along_m=False, rows=None, nthreads=0):
+    """Rows of all_gather along M of every rank's A @ B + bias, (M*W, N) float64.
+
+    peers: W-1 fp16 (M, N) buffers standing in for the other ranks' results,
+    in rank order without this rank."""
+    A, B = _u16(A), _u16(B)
+    M, K = A.shape
+    N = B.shape[1]
+    assert len(peers) == W - 1 and 0 <= rank < W
+    peers = [_u16(p) for p in peers]
+    m0, m1 = rows if rows is not None else (0, M * W)
+    bias = None if bias is None else _u16(bias)
+    out = np.empty((m1 - m0, N), np.float64)
+    pp = _ptr_array(peers) if peers else None
+    _load().oracle_matmul_all_gather(_p16(A), _p16(B), _p16(bias), _bias_mode(bias, bias_along_m),
+                                     pp, W, rank, M, N, K, m0, m1, out.ctypes.data_as(_f64p), nthreads)
+    return out
+
+
+def all_gather_flat(bufs) -> np.ndarray:
+    """all_gather of W flat fp16 buffers of n elements: their concatenation in rank order."""
+    bufs = [_u16(b).reshape(-1) for b in bufs]
+    n = bufs[0].size
+    out = np.empty(len(bufs) * n, np.uint16)
+    _load().oracle_all_gather_flat(_ptr_array(bufs), len(bufs), n, _p16(out))
+    return out
+
+
+def reduce_scatter_flat(bufs, rank) -> np.ndarray:
+    """This rank's n/W slice of the elementwise sum of W flat fp16 buffers, float64."""
+    bufs = [_u16(b).reshape(-1) for b in bufs]
+    W, n = len(bufs), bufs[0].size
+    assert n % W == 0 and 0 <= rank < W
+    out = np.empty(n // W, np.float64)
+    _load().oracle_reduce_scatter_flat(_ptr_array(bufs), W, n, rank, out.ctypes.data_as(_f64p))
+    return out
+
+
+def all_to_all_flat(bufs, rank) -> np.ndarray:
+    """Block j of the result is block `rank` of rank j's buffer (W blocks of n/W)."""
+    bufs = [_u16(b).reshape(-1) for b in bufs]
+    W, n = len(bufs), bufs[0].size
+    assert n % W == 0 and 0 <= rank < W
+    out = np.empty(n, np.uint16)
+    _load().oracle_all_to_all_flat(_ptr_array(bufs), W, n, rank, _p16(out))
+    return out
+
+
+def broadcast_flat(bufs, root) -> np.ndarray:
+    """The root rank's buffer."""
+    bufs = [_u16(b).reshape(-1) for b in bufs]
+    assert 0 <= root < len(bufs)
+    out = np.empty(bufs[0].size, np.uint16)
+    _load().oracle_broadcast_flat(_ptr_array(bufs), len(bufs), bufs[0].size, root, _p16(out))
+    return out

@@ -245,3 +245,57 @@ extern "C" void oracle_matmul_all_reduce(
       for (int64_t n = 0; n < N; ++n)
         out[(m - m0) * N + n] += oracle_f16_decode(partials[p][m * N + n]);
 }
+
+extern "C" void oracle_matmul_all_gather(
+    const uint16_t* A, const uint16_t* B, const uint16_t* bias, int bias_mode,
+    const uint16_t* const* peers, int W, int rank, int64_t M, int64_t N,
+    int64_t K, int64_t m0, int64_t m1, double* out, int nthreads) {
+  /* output row r belongs to the block of rank r / M; this rank's block is
+   * its own A @ B + bias, every other block is that rank's stand-in result,
+   * peers being listed in rank order without this rank */
+  for (int64_t r = m0; r < m1; ++r) {
+    const int64_t q = r / M, row = r - q * M;
+    double* o = out + (r - m0) * N;
+    if (q == rank) {
+      oracle_gemm_bias(A, K, B, N, bias, bias_mode, K, row, row + 1, 0, N, o,
+                       nthreads);
+    } else {
+      const uint16_t* src = peers[q < rank ? q : q - 1] + row * N;
+      for (int64_t n = 0; n < N; ++n) o[n] = oracle_f16_decode(src[n]);
+    }
+  }
+  (void)W;
+}
+
+/* ------------------------------------------------- flat collectives */
+
+extern "C" void oracle_all_gather_flat(const uint16_t* const* bufs, int W,
+                                       int64_t n, uint16_t* out) {
+  for (int w = 0; w < W; ++w)
+    for (int64_t i = 0; i < n; ++i) out[(int64_t)w * n + i] = bufs[w][i];
+}
+
+extern "C" void oracle_reduce_scatter_flat(const uint16_t* const* bufs, int W,
+                                           int64_t n, int rank, double* out) {
+  const int64_t part = n / W;
+  for (int64_t i = 0; i < part; ++i) {
+    double s = 0.0;
+    for (int w = 0; w < W; ++w)
+      s += oracle_f16_decode(bufs[w][(int64_t)rank * part + i]);
+    out[i] = s;
+  }
+}
+
+extern "C" void oracle_all_to_all_flat(const uint16_t* const* bufs, int W,
+                                       int64_t n, int rank, uint16_t* out) {
+  const int64_t part = n / W;
+  for (int j = 0; j < W; ++j)
+    for (int64_t i = 0; i < part; ++i)
+      out[(int64_t)j * part + i] = bufs[j][(int64_t)rank * part + i];
+}
+
+extern "C" void oracle_broadcast_flat(const uint16_t* const* bufs, int W,
+                                      int64_t n, int root, uint16_t* out) {
+  (void)W;
+  for (int64_t i = 0; i < n; ++i) out[i] = bufs[root][i];
+}

@@ -8,10 +8,12 @@
  *
  * Sources (the pages this oracle is written from):
  *   [DOCS]  Iris docs, "Fused Communication and Compute Operations":
- *           entries matmul_all_reduce, all_gather_matmul, matmul_reduce_scatter.
+ *           entries matmul_all_reduce, all_gather_matmul, matmul_all_gather,
+ *           matmul_reduce_scatter.
  *   [PR544] ROCm/iris pull request "Add iris.concurrent (concurrent,
  *           independent, fused comm+gemm)": description and review answer
- *           (an independent GEMM running beside a collective).
+ *           (an independent GEMM running beside a collective: all_gather,
+ *           all_reduce, reduce_scatter, all_to_all or broadcast).
  *
  * Conventions: fp16 values are IEEE-754 binary16 bit patterns in uint16_t.
  * Every matrix is row-major and contiguous unless a leading dimension is
@@ -103,6 +105,38 @@ void oracle_matmul_all_reduce(const uint16_t* A, const uint16_t* B,
                               const uint16_t* const* partials, int W,
                               int64_t M, int64_t N, int64_t K, int64_t m0,
                               int64_t m1, double* out, int nthreads);
+
+/*
+ * matmul_all_gather local share (rank `rank` of W): the (M*W x N) output is
+ * all_gather along M of every rank's A @ B + bias; this rank's block (rows
+ * [rank*M, (rank+1)*M)) is computed here, the other blocks are the W-1
+ * stand-in results `peers` (host pointers, each M x N fp16) in rank order
+ * with this rank skipped. Rows [m0, m1) of the output, as doubles (the peer
+ * rows decoded exactly).                                       [DOCS]
+ */
+void oracle_matmul_all_gather(const uint16_t* A, const uint16_t* B,
+                              const uint16_t* bias, int bias_mode,
+                              const uint16_t* const* peers, int W, int rank,
+                              int64_t M, int64_t N, int64_t K, int64_t m0,
+                              int64_t m1, double* out, int nthreads);
+
+/*
+ * The collectives of an independent GEMM + collective, local share of rank
+ * `rank` of W, each rank holding a buffer of n fp16 elements (bufs: W host
+ * pointers in rank order, this rank's own buffer included).     [PR544]
+ *   all_gather:     out[w*n + i] = bufs[w][i]                 (W*n, bit copy)
+ *   reduce_scatter: out[i] = sum_w bufs[w][rank*n/W + i]      (n/W, double)
+ *   all_to_all:     out[j*n/W + i] = bufs[j][rank*n/W + i]    (n, bit copy)
+ *   broadcast:      out[i] = bufs[root][i]                    (n, bit copy)
+ * (all_reduce is oracle_sum.) reduce_scatter and all_to_all need n % W == 0.
+ */
+void oracle_all_gather_flat(const uint16_t* const* bufs, int W, int64_t n, uint16_t* out);
+void oracle_reduce_scatter_flat(const uint16_t* const* bufs, int W, int64_t n, int rank,
+                                double* out);
+void oracle_all_to_all_flat(const uint16_t* const* bufs, int W, int64_t n, int rank,
+                            uint16_t* out);
+void oracle_broadcast_flat(const uint16_t* const* bufs, int W, int64_t n, int root,
+                           uint16_t* out);
 
 /* Number of threads a call with nthreads <= 0 uses on this host. */
 int oracle_default_threads(void);

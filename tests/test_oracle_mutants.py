@@ -17,7 +17,8 @@ from oracle import build as obuild
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.cpp")
-PINS = ["tests/test_oracle_fp16.py", "tests/test_oracle_ops.py", "tests/test_oracle_golden.py"]
+PINS = ["tests/test_oracle_fp16.py", "tests/test_oracle_ops.py", "tests/test_oracle_golden.py",
+        "tests/test_oracle_collectives.py"]
 
 MUTANTS = {
     "dropped_bias": ("acc[j] += bias_value(bias, bias_mode, m, n0 + j);", "(void)0;"),
@@ -34,6 +35,13 @@ MUTANTS = {
     "subnormal_scale": ("mag = std::ldexp((double)frac, -24);", "mag = std::ldexp((double)frac, -23);"),
     "exponent_bias": ("const int be = e + 15;", "const int be = e + 14;"),
     "row_bias_offset": ("bias_rows.assign(bias + m0, bias + m1);", "bias_rows.assign(bias, bias + (m1 - m0));"),
+    "mmag_peer_order": ("peers[q < rank ? q : q - 1]", "peers[(W - 2) - (q < rank ? q : q - 1)]"),
+    "mmag_own_block": ("if (q == rank) {", "if (q == 0) {"),
+    "ag_flat_order": ("out[(int64_t)w * n + i] = bufs[w][i];", "out[(int64_t)(W - 1 - w) * n + i] = bufs[w][i];"),
+    "rs_flat_slice": ("s += oracle_f16_decode(bufs[w][(int64_t)rank * part + i]);", "s += oracle_f16_decode(bufs[w][i]);"),
+    "a2a_source_block": ("out[(int64_t)j * part + i] = bufs[j][(int64_t)rank * part + i];",
+                         "out[(int64_t)j * part + i] = bufs[j][(int64_t)j * part + i];"),
+    "bcast_root": ("for (int64_t i = 0; i < n; ++i) out[i] = bufs[root][i];", "for (int64_t i = 0; i < n; ++i) out[i] = bufs[0][i];"),
 }
 
 
