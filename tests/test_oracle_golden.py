@@ -44,6 +44,15 @@ def test_golden(path):
         got = oracle.gemm_bias(h(g["A"]), h(g["B"]), bias, bias_along_m=along_m)
         comm = oracle.all_reduce([h(x) for x in g["comm_in"]])
         assert np.array_equal(comm, np.asarray(g["expected_comm"], np.float64))
+    elif op == "matmul_all_gather":
+        got = oracle.matmul_all_gather(h(g["A"]), h(g["B"]), [h(p) for p in g["peers"]], g["W"],
+                                       rank=g["rank"], bias=bias, bias_along_m=along_m)
+    elif op == "all_to_all":
+        bufs = [h(b) for b in g["bufs"]]
+        for r in (0, 1):
+            got_r = oracle.all_to_all_flat(bufs, r).view(np.float16).astype(np.float64)
+            assert np.array_equal(got_r, np.asarray(g[f"expected_rank{r}"], np.float64))
+        return
     else:
         raise AssertionError(op)
     assert np.array_equal(got, np.asarray(g["expected"], np.float64))
