@@ -30,13 +30,19 @@ LIB_PATH = os.path.join(_HERE, "libiris_local.so")
 IRIS_MAX_W = 16
 IRIS_MODE_FUSED = 0
 IRIS_MODE_SEQUENTIAL = 1
+IRIS_MODE_TWO_STREAM = 2
 IRIS_FLAG_NO_STEAL = 1
 IRIS_FLAG_BIAS_ALONG_M = 2
 IRIS_OP_AG_MM = 1
 IRIS_OP_MM_RS = 2
 IRIS_OP_MM_AR = 3
 IRIS_OP_CONCURRENT = 4
+IRIS_OP_MM_AG = 5
 IRIS_COLL_ALL_REDUCE = 1
+IRIS_COLL_ALL_GATHER = 2
+IRIS_COLL_REDUCE_SCATTER = 3
+IRIS_COLL_ALL_TO_ALL = 4
+IRIS_COLL_BROADCAST = 5
 
 STATUS = {
     0: "IRIS_OK", 1: "IRIS_ERR_INVALID_ARG", 2: "IRIS_ERR_UNSUPPORTED", 3: "IRIS_ERR_CONFIG",
@@ -79,7 +85,7 @@ class _OpArgs(ctypes.Structure):
     _fields_ = [
         ("op", ctypes.c_int32), ("C", ctypes.c_void_p), ("out", ctypes.c_void_p),
         ("A", ctypes.c_void_p), ("srcs", ctypes.POINTER(ctypes.c_void_p)),
-        ("W", ctypes.c_int32), ("rank", ctypes.c_int32), ("B", ctypes.c_void_p),
+        ("W", ctypes.c_int32), ("rank", ctypes.c_int32), ("collective", ctypes.c_int32), ("B", ctypes.c_void_p),
         ("bias", ctypes.c_void_p), ("M", ctypes.c_int64), ("N", ctypes.c_int64),
         ("K", ctypes.c_int64), ("comm_elems", ctypes.c_int64), ("cfg", _Config),
     ]
@@ -104,7 +110,8 @@ def _load() -> ctypes.CDLL:
         "iris_ag_mm": [vp, vp, vpp, i32, vp, vp, i64, i64, i64, cfgp, vp, sz, vp],
         "iris_mm_rs_local": [vp, vp, vp, vp, vp, vpp, i32, i32, i64, i64, i64, cfgp, vp, sz, vp],
         "iris_mm_ar_local": [vp, vp, vp, vp, vp, vpp, i32, i64, i64, i64, cfgp, vp, sz, vp],
-        "iris_concurrent": [vp, vp, vp, vp, i64, i64, i64, i32, vp, vpp, i32, i64, cfgp, vp, sz, vp],
+        "iris_concurrent": [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vpp, i32, i64, cfgp, vp, sz, vp],
+        "iris_mm_ag_local": [vp, vp, vp, vp, vpp, i32, i32, i64, i64, i64, cfgp, vp, sz, vp],
         "iris_grid_size": [ctypes.c_int32, cfgp],
         "iris_tune_gemm_wgs": [ctypes.POINTER(_OpArgs), ctypes.POINTER(i32), i32, i32,
                                ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float), vp],
@@ -218,17 +225,43 @@ def iris_mm_ar_local(out, C, A, B, partials, W, bias=None, config=None, workspac
                                  M, N, K, _cfg(config), ws, wsb, _stream(stream)))
 
 
-def iris_concurrent(C, A, B, comm_out, comm_in, bias=None, collective=IRIS_COLL_ALL_REDUCE,
+_COMM_OUT_LEN = {
+    IRIS_COLL_ALL_REDUCE: lambda n, W: n, IRIS_COLL_ALL_GATHER: lambda n, W: W * n,
+    IRIS_COLL_REDUCE_SCATTER: lambda n, W: n // W, IRIS_COLL_ALL_TO_ALL: lambda n, W: n,
+    IRIS_COLL_BROADCAST: lambda n, W: n,
+}
+
+
+def iris_concurrent(C, A, B, comm_out, comm_in, bias=None, collective=IRIS_COLL_ALL_REDUCE, rank=0,
                     config=None, workspace=None, stream=None):
-    """C = A @ B + bias, and independently comm_out = sum(comm_in) (all_reduce local share)."""
+    """C = A @ B + bias, and independently the local share of `collective`
+    over the W buffers comm_in (every rank's buffer, own included) into
+    comm_out; `rank` is this rank (the root for broadcast)."""
     M, K = _shape2(A, "A")
     N = _shape2(B, "B")[1]
-    n = comm_out.numel()
+    n = comm_in[0].numel()
+    W = len(comm_in)
+    if collective in _COMM_OUT_LEN and comm_out.numel() != _COMM_OUT_LEN[collective](n, W):
+        raise ValueError(f"comm_out has {comm_out.numel()} elements, collective {collective} of {W} "
+                         f"buffers of {n} writes {_COMM_OUT_LEN[collective](n, W)}")
     ws, wsb = _ws(workspace)
     _check(_lib.iris_concurrent(_ptr(C, "C"), _ptr(A, "A"), _ptr(B, "B"), _ptr(bias, "bias", True),
-                                M, N, K, collective, _ptr(comm_out, "comm_out"),
-                                _ptr_array(comm_in, "comm_in"), len(comm_in), n, _cfg(config),
+                                M, N, K, collective, rank, _ptr(comm_out, "comm_out"),
+                                _ptr_array(comm_in, "comm_in"), W, n, _cfg(config),
                                 ws, wsb, _stream(stream)))
+
+
+def iris_mm_ag_local(out, A, B, peers, W, rank=0, bias=None, config=None, workspace=None, stream=None):
+    """matmul_all_gather local share: out (M*W, N) holds every rank's A @ B + bias
+    along M; this rank's block is computed, the W-1 `peers` (M, N) are copied."""
+    M, K = _shape2(A, "A")
+    N = _shape2(B, "B")[1]
+    if out.numel() != M * W * N:
+        raise ValueError(f"out has {out.numel()} elements, expected {M * W} x {N}")
+    ws, wsb = _ws(workspace)
+    _check(_lib.iris_mm_ag_local(_ptr(out, "out"), _ptr(A, "A"), _ptr(B, "B"), _ptr(bias, "bias", True),
+                                 _ptr_array(peers, "peers"), W, rank, M, N, K, _cfg(config), ws, wsb,
+                                 _stream(stream)))
 
 
 # ------------------------------------------------------------------- helpers
@@ -246,7 +279,7 @@ def iris_grid_size(config=None, op=IRIS_OP_AG_MM) -> int:
 
 
 def iris_tune_gemm_wgs(op, candidates, reps=5, config=None, stream=None, *, C=None, out=None, A=None,
-                       srcs=(), W=1, rank=0, B=None, bias=None, M=0, N=0, K=0, comm_elems=0):
+                       srcs=(), W=1, rank=0, collective=0, B=None, bias=None, M=0, N=0, K=0, comm_elems=0):
     """Sweep gemm_wgs over `candidates` (the static default is always added),
     cache and return (best, {candidate: median ms})."""
     keep = _ptr_array(list(srcs), "srcs")
@@ -256,7 +289,7 @@ def iris_tune_gemm_wgs(op, candidates, reps=5, config=None, stream=None, *, C=No
     a.out = _ptr(out, "out", True)
     a.A = _ptr(A, "A", True)
     a.srcs = ctypes.cast(keep, ctypes.POINTER(ctypes.c_void_p))
-    a.W, a.rank = W, rank
+    a.W, a.rank, a.collective = W, rank, collective
     a.B = _ptr(B, "B", True)
     a.bias = _ptr(bias, "bias", True)
     a.M, a.N, a.K, a.comm_elems = M, N, K, comm_elems

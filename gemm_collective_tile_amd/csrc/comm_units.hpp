@@ -8,11 +8,17 @@
 //   `rows_u` rows of one shard (a slice of one GEMM row block). Bit copy.
 //
 //   reduce (same page, matmul_reduce_scatter and matmul_all_reduce; the
-//   all_reduce beside an independent GEMM of the iris.concurrent PR):
-//   out = own + sum of the other ranks' partial buffers, in that order,
-//   accumulated in fp32 and rounded once to fp16. A unit is a rectangle of
-//   rows x columns (reduce_scatter / matmul_all_reduce) or a flat chunk
-//   (concurrent all_reduce).
+//   all_reduce and reduce_scatter beside an independent GEMM of the
+//   iris.concurrent PR): out = own + sum of the other ranks' partial
+//   buffers, in that order, accumulated in fp32 and rounded once to fp16. A
+//   unit is a rectangle of rows x columns (reduce_scatter / matmul_all_reduce)
+//   or a flat chunk (the concurrent collectives).
+//
+//   block copy (the all_gather, all_to_all and broadcast beside an
+//   independent GEMM of the iris.concurrent PR; the peer blocks of
+//   matmul_all_gather on the docs page): source w, a contiguous block of
+//   `blk` elements, lands at block position dst_blk[w] of the output. A unit
+//   is a flat chunk of one block. Bit copy.
 //
 // A CU moves only a few tens of GB/s, bounded by the memory requests its
 // waves keep in flight, so each thread issues all loads of a batch (up to 8
@@ -42,9 +48,13 @@ struct CommArgs {
   int32_t ncols;          // N_local (RS) or N (AR): row length of src and dst
   int32_t comm_bn;        // columns per unit
   int32_t n_cc;           // column chunks per row slice
-  // flat all_reduce
+  // flat all_reduce / reduce_scatter
   int64_t elems;
   int32_t chunk;
+  // block copy: W sources of blk elements, source w to block dst_blk[w]
+  int64_t blk;
+  int32_t n_chunk;        // chunks per block
+  int32_t dst_blk[kMaxW];
   int32_t M, BM;
   int32_t rows_u;         // rows per unit (divides BM)
   int32_t n_sub;          // units per row block along M: BM / rows_u
@@ -195,6 +205,31 @@ __device__ void reduce_flat_unit(const CommArgs& a, int u) {
 #pragma unroll
     for (int v = 0; v < U; ++v)
       if (ok[v]) st16_nt(a.dst + idx[v], round8(acc[v]));
+  }
+}
+
+// ------------------------------------------------------------- block copy
+// Unit (w, c): elements [c*chunk, min((c+1)*chunk, blk)) of source w.
+template <int U>
+__device__ void copy_block_unit(const CommArgs& a, int w, int c) {
+  const int64_t e0 = (int64_t)c * a.chunk;
+  const int64_t n = min((int64_t)a.chunk, a.blk - e0);
+  if (n <= 0) return;
+  const uint32_t total = (uint32_t)(n >> 3);
+  const f16* src = a.src[w] + e0;
+  f16* dst = a.dst + (int64_t)a.dst_blk[w] * a.blk + e0;
+  for (uint32_t base = threadIdx.x; base < total; base += kThreads * U) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t i = base + u * kThreads;
+      if (i < total) v[u] = ld16_nt(src + (int64_t)i * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t i = base + u * kThreads;
+      if (i < total) st16_nt(dst + (int64_t)i * 8, v[u]);
+    }
   }
 }
 

@@ -44,25 +44,6 @@ __device__ __forceinline__ void buf_store16_coherent(__amdgpu_buffer_rsrc_t r, u
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kPolicySc1);
 }
 
-// The same resource as four dwords, for use as an inline-asm operand.
-__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)base;
-  u32x4 r;
-  r[0] = (uint32_t)a;
-  r[1] = (uint32_t)(a >> 32) & 0xffffu;  // stride 0
-  r[2] = bytes;
-  r[3] = (uint32_t)kRsrcWord3;
-  return r;
-}
-
-// LDS DMA: lane l's 16 bytes at buffer offset `off` land at LDS byte address
-// lds_addr + 16 l (default caching). Issued through inline asm so that the
-// compiler does not make every later LDS read wait for it: the caller orders
-// it with explicit vmcnt waits and barriers.
-__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds_addr, uint32_t off) {
-  asm volatile("buffer_load_dwordx4 %1, %2, 0 offen lds" ::"{m0}"(lds_addr), "v"(off), "s"(rsrc));
-}
-
 // ----------------------------------------------------------- plain vectors
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }

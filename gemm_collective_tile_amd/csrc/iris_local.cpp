@@ -169,6 +169,7 @@ int iris_op_to_kind(int op) {
     case IRIS_OP_MM_RS: return iris::OP_RS;
     case IRIS_OP_MM_AR: return iris::OP_ARMM;
     case IRIS_OP_CONCURRENT: return iris::OP_CONC_AR;
+    case IRIS_OP_MM_AG: return iris::OP_CONC_COPY;
   }
   return -1;
 }
@@ -198,7 +199,7 @@ int resolve_static(const iris_config_t* cfg, Resolved* r) {
     return fail(IRIS_ERR_CONFIG, "comm_block_m must divide block_m (%d does not divide %d)", r->comm_bm, r->bm);
   if (r->comm_bn % 8 != 0) return fail(IRIS_ERR_CONFIG, "comm_block_n must be a multiple of 8 (got %d)", r->comm_bn);
   if (r->comm_chunk % 2048 != 0) return fail(IRIS_ERR_CONFIG, "comm_chunk must be a multiple of 2048 (got %d)", r->comm_chunk);
-  if (r->mode != IRIS_MODE_FUSED && r->mode != IRIS_MODE_SEQUENTIAL)
+  if (r->mode != IRIS_MODE_FUSED && r->mode != IRIS_MODE_SEQUENTIAL && r->mode != IRIS_MODE_TWO_STREAM)
     return fail(IRIS_ERR_CONFIG, "unknown mode %d", r->mode);
   if (r->flags & ~(IRIS_FLAG_NO_STEAL | IRIS_FLAG_BIAS_ALONG_M))
     return fail(IRIS_ERR_CONFIG, "unknown flag bits 0x%x", r->flags);
@@ -219,7 +220,7 @@ int resolve_device(Resolved* r, int kind, const DevInfo& di, const std::string& 
     }
     r->gemm_wgs = (tuned > 0 && tuned < r->grid) ? tuned : (r->grid * 7) / 8;
   }
-  if (r->mode == IRIS_MODE_FUSED && (r->gemm_wgs < 1 || r->gemm_wgs > r->grid - 1))
+  if (r->mode != IRIS_MODE_SEQUENTIAL && (r->gemm_wgs < 1 || r->gemm_wgs > r->grid - 1))
     return fail(IRIS_ERR_CONFIG, "gemm_wgs %d outside [1, %d] for a grid of %d workgroups", r->gemm_wgs,
                 r->grid - 1, r->grid);
   return IRIS_OK;
@@ -323,7 +324,9 @@ int check_gemm_dims(int64_t M, int64_t N, int64_t K) {
 
 // ---------------------------------------------------------------- launch
 struct OpDesc {
-  int kind;  // iris::OpKind
+  int kind;        // iris::OpKind
+  int iris_op;     // IRIS_OP_* (tuning cache key)
+  int collective;  // IRIS_COLL_* of the concurrent op, else 0
   void* C;
   void* out;
   const void* A;
@@ -335,23 +338,56 @@ struct OpDesc {
   int64_t M, N, K;  // K = full contraction length
   int64_t K_local;
   int64_t comm_elems;
+  // flat comm units of the independent ops: sources W (reduce) or nsrc (copy)
+  int64_t src_off;      // element offset applied to every source
+  int64_t flat_elems;   // reduce: elements of the result; copy: block length
+  int nsrc;             // copy: number of source blocks
+  int dst_blk[IRIS_MAX_W];
 };
+
+// The second stream and fork/join events of the two-stream mode, per
+// (device, caller stream), created on first use.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::map<std::pair<int, void*>, SideStream> g_side;
+
+int get_side_stream(int dev, void* stream, SideStream** out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  SideStream& ss = g_side[{dev, stream}];
+  if (!ss.s) {
+    hipError_t e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      if (ss.join) (void)hipEventDestroy(ss.join);
+      if (ss.fork) (void)hipEventDestroy(ss.fork);
+      if (ss.s) (void)hipStreamDestroy(ss.s);
+      ss = SideStream{};
+      return hip_fail(e, "creating the two-stream mode's stream and events");
+    }
+  }
+  *out = &ss;
+  return IRIS_OK;
+}
 
 int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_bytes, void* stream,
         Resolved* used = nullptr) {
   Resolved r{};
   int st = resolve_static(cfg, &r);
   if (st) return st;
+  if (r.mode == IRIS_MODE_TWO_STREAM && d.kind != iris::OP_CONC_AR && d.kind != iris::OP_CONC_COPY)
+    return fail(IRIS_ERR_CONFIG,
+                "two-stream mode needs an op whose GEMM and collective are independent "
+                "(iris_concurrent, iris_mm_ag_local)");
   int dev = 0;
   DevInfo di;
   st = current_device(&dev, &di);
   if (st) return st;
-  const int iris_op = d.kind == iris::OP_AG ? IRIS_OP_AG_MM
-                      : d.kind == iris::OP_RS ? IRIS_OP_MM_RS
-                      : d.kind == iris::OP_ARMM ? IRIS_OP_MM_AR
-                                                : IRIS_OP_CONCURRENT;
-  const std::string key =
-      cache_key(di.arch, iris_op, d.M, d.N, d.kind == iris::OP_AG ? d.K_local : d.K, d.W, r.bm, r.bn, r.bk, r.gm);
+  // the concurrent op's collectives tune apart: fold the collective into the op
+  const std::string key = cache_key(di.arch, d.iris_op * 16 + d.collective, d.M, d.N,
+                                    d.kind == iris::OP_AG ? d.K_local : d.K, d.W, r.bm, r.bn, r.bk, r.gm);
   st = resolve_device(&r, d.kind, di, key);
   if (st) return st;
   if (r.comm_bm <= 0) {
@@ -433,11 +469,23 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
     }
     case iris::OP_CONC_AR:
       c.W = d.W;
-      for (int s = 0; s < d.W; ++s) c.src[s] = (const iris::f16*)d.srcs[s];
+      for (int s = 0; s < d.W; ++s) c.src[s] = (const iris::f16*)d.srcs[s] + d.src_off;
       c.dst = (iris::f16*)d.out;
-      c.elems = d.comm_elems;
+      c.elems = d.flat_elems;
       c.chunk = r.comm_chunk;
-      t_comm = (d.comm_elems + r.comm_chunk - 1) / r.comm_chunk;
+      t_comm = (d.flat_elems + r.comm_chunk - 1) / r.comm_chunk;
+      break;
+    case iris::OP_CONC_COPY:
+      c.W = d.nsrc;
+      for (int s = 0; s < d.nsrc; ++s) {
+        c.src[s] = (const iris::f16*)d.srcs[s] + d.src_off;
+        c.dst_blk[s] = d.dst_blk[s];
+      }
+      c.dst = (iris::f16*)d.out;
+      c.blk = d.flat_elems;
+      c.chunk = r.comm_chunk;
+      c.n_chunk = (int)((d.flat_elems + r.comm_chunk - 1) / r.comm_chunk);
+      t_comm = (int64_t)d.nsrc * c.n_chunk;
       break;
   }
   if (t_comm > (1 << 30))
@@ -456,12 +504,39 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
 
   hipError_t e = hipSuccess;
   int comm_grid = 0;
+  int gemm_grid = r.grid;
   if (r.mode == IRIS_MODE_FUSED) {
     p.op = d.kind;
     p.fused = 1;
     p.gemm_wgs = r.gemm_wgs;
     e = iris::launch_persistent(p, r.bm, r.bn, r.grid, s);
     if (e != hipSuccess) return hip_fail(e, "fused launch");
+  } else if (r.mode == IRIS_MODE_TWO_STREAM) {
+    // fork: the comm kernel runs on the side stream after everything already
+    // queued on the caller's stream; join: the caller's stream continues only
+    // after it. The GEMM kernel takes gemm_wgs workgroups, the comm kernel
+    // the rest of the CUs; neither waits on the other.
+    SideStream* ss = nullptr;
+    st = get_side_stream(dev, stream, &ss);
+    if (st) return st;
+    Params pg = p;
+    pg.op = iris::OP_GEMM;
+    pg.fused = 0;
+    pg.T_comm = 0;
+    pg.gemm_wgs = r.gemm_wgs;
+    pg.xcd_q = std::max(1, r.gemm_wgs / iris::kXcds);
+    Params pc = p;
+    pc.op = d.kind;
+    pc.fused = 0;
+    gemm_grid = r.gemm_wgs;
+    comm_grid = std::min((r.grid - r.gemm_wgs) * 4, kMaxGrid);
+    e = hipEventRecord(ss->fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
+    if (e == hipSuccess) e = iris::launch_comm_only(pc, comm_grid, ss->s);
+    if (e == hipSuccess) e = iris::launch_persistent(pg, r.bm, r.bn, gemm_grid, s);
+    if (e == hipSuccess) e = hipEventRecord(ss->join, ss->s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, ss->join, 0);
+    if (e != hipSuccess) return hip_fail(e, "two-stream launch");
   } else {
     // unfused baseline: the comm kernel and the GEMM kernel each get the
     // whole GPU, in dependency order (gather before GEMM; GEMM before reduce)
@@ -485,7 +560,7 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
   }
   {
     std::lock_guard<std::mutex> lk(g_mu);
-    g_last[ws] = LastLaunch{dev, r.grid, comm_grid, r.mode == IRIS_MODE_FUSED, 0};
+    g_last[ws] = LastLaunch{dev, gemm_grid, comm_grid, r.mode == IRIS_MODE_FUSED, 0};
   }
   if (getenv("IRIS_LOCAL_DEBUG")) {
     e = hipStreamSynchronize(s);
@@ -531,6 +606,7 @@ int iris_ag_mm(void* C, void* A_gathered, const void* const* A_shards, int32_t W
   if ((st = check_gemm_dims(M, N, K_local * W))) return st;
   OpDesc d{};
   d.kind = iris::OP_AG;
+  d.iris_op = IRIS_OP_AG_MM;
   d.C = C;
   d.out = A_gathered;
   d.srcs = A_shards;
@@ -559,6 +635,7 @@ int iris_mm_rs_local(void* out, void* C, const void* A, const void* B, const voi
   if ((N / W) % 8 != 0) return fail(IRIS_ERR_ALIGNMENT, "N/W must be a multiple of 8 (got %lld)", (long long)(N / W));
   OpDesc d{};
   d.kind = iris::OP_RS;
+  d.iris_op = IRIS_OP_MM_RS;
   d.C = C;
   d.out = out;
   d.A = A;
@@ -585,6 +662,7 @@ int iris_mm_ar_local(void* out, void* C, const void* A, const void* B, const voi
   if ((st = check_gemm_dims(M, N, K))) return st;
   OpDesc d{};
   d.kind = iris::OP_ARMM;
+  d.iris_op = IRIS_OP_MM_AR;
   d.C = C;
   d.out = out;
   d.A = A;
@@ -599,35 +677,109 @@ int iris_mm_ar_local(void* out, void* C, const void* A, const void* B, const voi
 }
 
 int iris_concurrent(void* C, const void* A, const void* B, const void* bias, int64_t M, int64_t N, int64_t K,
-                    int32_t collective, void* comm_out, const void* const* comm_in, int32_t W,
+                    int32_t collective, int32_t rank, void* comm_out, const void* const* comm_in, int32_t W,
                     int64_t comm_elems, const iris_config_t* cfg, void* workspace, size_t workspace_bytes,
                     void* stream) {
   g_msg.clear();
-  if (collective != IRIS_COLL_ALL_REDUCE)
-    return fail(IRIS_ERR_UNSUPPORTED, "collective %d is not supported (only IRIS_COLL_ALL_REDUCE)", collective);
+  if (collective < IRIS_COLL_ALL_REDUCE || collective > IRIS_COLL_BROADCAST)
+    return fail(IRIS_ERR_UNSUPPORTED, "unknown collective %d", collective);
   if (W < 1 || W > IRIS_MAX_W) return fail(IRIS_ERR_INVALID_ARG, "W must be in [1, %d] (got %d)", IRIS_MAX_W, W);
+  const bool ranked = collective == IRIS_COLL_REDUCE_SCATTER || collective == IRIS_COLL_ALL_TO_ALL ||
+                      collective == IRIS_COLL_BROADCAST;
+  if (ranked && (rank < 0 || rank >= W)) return fail(IRIS_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, W);
   int st;
   if ((st = check_ptr(C, "C")) || (st = check_ptr(A, "A")) || (st = check_ptr(B, "B")) ||
       (st = check_ptr(bias, "bias", false)) || (st = check_ptr(comm_out, "comm_out")) ||
       (st = copy_ptrs(comm_in, W, "comm_in")))
     return st;
   if ((st = check_gemm_dims(M, N, K))) return st;
-  if (comm_elems <= 0) return fail(IRIS_ERR_INVALID_ARG, "comm_elems must be positive");
-  if (comm_elems % 8 != 0) return fail(IRIS_ERR_ALIGNMENT, "comm_elems must be a multiple of 8");
-  if (comm_elems > ((int64_t)1 << 40)) return fail(IRIS_ERR_UNSUPPORTED, "comm_elems too large");
+  const int64_t n = comm_elems;
+  if (n <= 0) return fail(IRIS_ERR_INVALID_ARG, "comm_elems must be positive");
+  if (n % 8 != 0) return fail(IRIS_ERR_ALIGNMENT, "comm_elems must be a multiple of 8");
+  if (n > ((int64_t)1 << 40)) return fail(IRIS_ERR_UNSUPPORTED, "comm_elems too large");
+  const bool split = collective == IRIS_COLL_REDUCE_SCATTER || collective == IRIS_COLL_ALL_TO_ALL;
+  if (split && n % (8 * (int64_t)W) != 0)
+    return fail(IRIS_ERR_ALIGNMENT, "comm_elems must be a multiple of 8 W for this collective (got %lld, W=%d)",
+                (long long)n, W);
   OpDesc d{};
-  d.kind = iris::OP_CONC_AR;
+  d.iris_op = IRIS_OP_CONCURRENT;
+  d.collective = collective;
   d.C = C;
   d.out = comm_out;
   d.A = A;
   d.srcs = comm_in;
   d.W = W;
+  d.rank = rank;
   d.B = B;
   d.bias = bias;
   d.M = M;
   d.N = N;
   d.K = K;
-  d.comm_elems = comm_elems;
+  d.comm_elems = n;
+  switch (collective) {
+    case IRIS_COLL_ALL_REDUCE:  // every element, every buffer
+      d.kind = iris::OP_CONC_AR;
+      d.flat_elems = n;
+      break;
+    case IRIS_COLL_REDUCE_SCATTER:  // this rank's n/W slice of every buffer
+      d.kind = iris::OP_CONC_AR;
+      d.src_off = (int64_t)rank * (n / W);
+      d.flat_elems = n / W;
+      break;
+    case IRIS_COLL_ALL_GATHER:  // buffer w -> block w of W n
+      d.kind = iris::OP_CONC_COPY;
+      d.nsrc = W;
+      d.flat_elems = n;
+      for (int w = 0; w < W; ++w) d.dst_blk[w] = w;
+      break;
+    case IRIS_COLL_ALL_TO_ALL:  // block `rank` of buffer j -> block j
+      d.kind = iris::OP_CONC_COPY;
+      d.nsrc = W;
+      d.src_off = (int64_t)rank * (n / W);
+      d.flat_elems = n / W;
+      for (int w = 0; w < W; ++w) d.dst_blk[w] = w;
+      break;
+    case IRIS_COLL_BROADCAST:  // the root's buffer
+      d.kind = iris::OP_CONC_COPY;
+      d.nsrc = 1;
+      d.srcs = comm_in + rank;
+      d.flat_elems = n;
+      d.dst_blk[0] = 0;
+      break;
+  }
+  return run(d, cfg, workspace, workspace_bytes, stream);
+}
+
+int iris_mm_ag_local(void* out, const void* A, const void* B, const void* bias, const void* const* peer_blocks,
+                     int32_t W, int32_t rank, int64_t M, int64_t N, int64_t K, const iris_config_t* cfg,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  g_msg.clear();
+  if (W < 1 || W > IRIS_MAX_W) return fail(IRIS_ERR_INVALID_ARG, "W must be in [1, %d] (got %d)", IRIS_MAX_W, W);
+  if (rank < 0 || rank >= W) return fail(IRIS_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, W);
+  int st;
+  if ((st = check_ptr(out, "out")) || (st = check_ptr(A, "A")) || (st = check_ptr(B, "B")) ||
+      (st = check_ptr(bias, "bias", false)) || (st = copy_ptrs(peer_blocks, W - 1, "peer_blocks")))
+    return st;
+  if ((st = check_gemm_dims(M, N, K))) return st;
+  if ((int64_t)W * M > (1 << 30)) return fail(IRIS_ERR_UNSUPPORTED, "M * W too large (limit 2^30)");
+  OpDesc d{};
+  d.kind = iris::OP_CONC_COPY;
+  d.iris_op = IRIS_OP_MM_AG;
+  // this rank's block of the output is the GEMM's C
+  d.C = (char*)out + (size_t)rank * (size_t)M * (size_t)N * 2;
+  d.out = out;
+  d.A = A;
+  d.srcs = peer_blocks;
+  d.W = W;
+  d.rank = rank;
+  d.B = B;
+  d.bias = bias;
+  d.M = M;
+  d.N = N;
+  d.K = K;
+  d.nsrc = W - 1;
+  d.flat_elems = M * N;
+  for (int p = 0; p < W - 1; ++p) d.dst_blk[p] = p < rank ? p : p + 1;
   return run(d, cfg, workspace, workspace_bytes, stream);
 }
 
@@ -683,8 +835,12 @@ int iris_tune_gemm_wgs(const iris_op_args_t* a, const int32_t* candidates, int32
         return iris_mm_ar_local(a->out, a->C, a->A, a->B, a->bias, a->srcs, a->W, a->M, a->N, a->K, &cfg, nullptr,
                                 0, stream);
       case IRIS_OP_CONCURRENT:
-        return iris_concurrent(a->C, a->A, a->B, a->bias, a->M, a->N, a->K, IRIS_COLL_ALL_REDUCE, a->out, a->srcs,
+        return iris_concurrent(a->C, a->A, a->B, a->bias, a->M, a->N, a->K,
+                               a->collective > 0 ? a->collective : IRIS_COLL_ALL_REDUCE, a->rank, a->out, a->srcs,
                                a->W, a->comm_elems, &cfg, nullptr, 0, stream);
+      case IRIS_OP_MM_AG:
+        return iris_mm_ag_local(a->out, a->A, a->B, a->bias, a->srcs, a->W, a->rank, a->M, a->N, a->K, &cfg,
+                                nullptr, 0, stream);
     }
     return fail(IRIS_ERR_INVALID_ARG, "unknown op %d", a->op);
   };
@@ -739,7 +895,8 @@ int iris_tune_gemm_wgs(const iris_op_args_t* a, const int32_t* candidates, int32
     Resolved r{};
     resolve_static(&cfg, &r);
     // AG keys on K_local (args->K), the other ops on K, as run() looks them up
-    save_cache_entry(cache_key(di.arch, a->op, a->M, a->N, a->K, a->W, r.bm, r.bn, r.bk, r.gm), best);
+    const int coll = a->op == IRIS_OP_CONCURRENT ? (a->collective > 0 ? a->collective : IRIS_COLL_ALL_REDUCE) : 0;
+    save_cache_entry(cache_key(di.arch, a->op * 16 + coll, a->M, a->N, a->K, a->W, r.bm, r.bn, r.bk, r.gm), best);
   }
   return IRIS_OK;
 }
@@ -842,6 +999,14 @@ int iris_finalize(void) {
   }
   g_ws.clear();
   g_last.clear();
+  for (auto& kv : g_side) {
+    (void)hipSetDevice(kv.first.first);
+    if (kv.second.s && hipStreamSynchronize(kv.second.s) != hipSuccess) status = IRIS_ERR_HIP;
+    if (kv.second.join) (void)hipEventDestroy(kv.second.join);
+    if (kv.second.fork) (void)hipEventDestroy(kv.second.fork);
+    if (kv.second.s && hipStreamDestroy(kv.second.s) != hipSuccess) status = IRIS_ERR_HIP;
+  }
+  g_side.clear();
   return status;
 }
 

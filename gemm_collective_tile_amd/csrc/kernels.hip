@@ -124,6 +124,9 @@ __device__ void run_comm_unit(const Params& p, int u) {
     reduce2d_unit<2>(c, pm, slice - pm * c.n_sub, u - slice * c.n_cc);
   } else if constexpr (OP == OP_CONC_AR) {
     reduce_flat_unit<2>(c, u);
+  } else if constexpr (OP == OP_CONC_COPY) {
+    const int w = u / c.n_chunk;
+    copy_block_unit<8>(c, w, u - w * c.n_chunk);
   }
 }
 
@@ -344,6 +347,7 @@ static hipError_t launch_op(const Params& p, int grid, hipStream_t s) {
     case OP_RS: return launch_tile<OP_RS, BM, BN>(p, grid, s);
     case OP_ARMM: return launch_tile<OP_ARMM, BM, BN>(p, grid, s);
     case OP_CONC_AR: return launch_tile<OP_CONC_AR, BM, BN>(p, grid, s);
+    case OP_CONC_COPY: return launch_tile<OP_CONC_COPY, BM, BN>(p, grid, s);
   }
   return hipErrorInvalidValue;
 }
@@ -375,6 +379,9 @@ hipError_t launch_comm_only(const Params& p, int grid, hipStream_t s) {
     case OP_CONC_AR:
       hipLaunchKernelGGL((comm_only_kernel<OP_CONC_AR>), dim3(grid), dim3(kThreads), 0, s, p);
       break;
+    case OP_CONC_COPY:
+      hipLaunchKernelGGL((comm_only_kernel<OP_CONC_COPY>), dim3(grid), dim3(kThreads), 0, s, p);
+      break;
     default:
       return hipErrorInvalidValue;
   }
@@ -398,6 +405,7 @@ static int occ_op(int op) {
     case OP_RS: return occ_tile<OP_RS, BM, BN>();
     case OP_ARMM: return occ_tile<OP_ARMM, BM, BN>();
     case OP_CONC_AR: return occ_tile<OP_CONC_AR, BM, BN>();
+    case OP_CONC_COPY: return occ_tile<OP_CONC_COPY, BM, BN>();
   }
   return -1;
 }

@@ -16,7 +16,9 @@ enum OpKind : int32_t {
   OP_AG = 1,          // comm: all_gather copy units; GEMM waits on row flags
   OP_RS = 2,          // comm: reduce_scatter units wait on GEMM tile flags
   OP_ARMM = 3,        // comm: matmul_all_reduce units wait on GEMM tile flags
-  OP_CONC_AR = 4,     // comm: independent flat all_reduce units
+  OP_CONC_AR = 4,     // comm: independent flat reduce units (all_reduce, reduce_scatter)
+  OP_CONC_COPY = 5,   // comm: independent block copies (all_gather, all_to_all,
+                      // broadcast, matmul_all_gather's peer blocks)
 };
 
 // Workspace layout: first uint64 stamps[kMaxGrid][4] written by the

@@ -79,6 +79,14 @@ typedef enum iris_status {
 #define IRIS_MODE_SEQUENTIAL 1 /* comm kernel and GEMM kernel, one after the
                                   other on the same stream, each on the whole
                                   GPU (the unfused baseline) */
+#define IRIS_MODE_TWO_STREAM 2 /* GEMM kernel on gemm_wgs workgroups on the
+                                  caller's stream, comm kernel beside it on a
+                                  second stream of the library's; only for ops
+                                  whose GEMM and collective are independent
+                                  (iris_concurrent, iris_mm_ag_local), others
+                                  give IRIS_ERR_CONFIG ([PR544]: mode
+                                  "concurrent", separate persistent kernels on
+                                  different streams) */
 
 /* config flags */
 #define IRIS_FLAG_NO_STEAL 1     /* workgroups stay on their first queue */
@@ -89,9 +97,15 @@ typedef enum iris_status {
 #define IRIS_OP_MM_RS 2
 #define IRIS_OP_MM_AR 3
 #define IRIS_OP_CONCURRENT 4
+#define IRIS_OP_MM_AG 5
 
-/* collectives for iris_concurrent */
+/* collectives for iris_concurrent ([PR544] description: all_gather,
+ * all_reduce, reduce_scatter, all_to_all, broadcast) */
 #define IRIS_COLL_ALL_REDUCE 1
+#define IRIS_COLL_ALL_GATHER 2
+#define IRIS_COLL_REDUCE_SCATTER 3
+#define IRIS_COLL_ALL_TO_ALL 4
+#define IRIS_COLL_BROADCAST 5
 
 /*
  * Tuning knobs ([PR544]: the GEMM/comm split gemm_wgs and the GEMM tile;
@@ -112,9 +126,11 @@ typedef enum iris_status {
  *                     shard (copy) or 32 KiB per buffer (reduce).
  *   comm_block_n      columns per reduce unit (reduce_scatter and
  *                     matmul_all_reduce), multiple of 8. Default block_n.
- *   comm_chunk        elements per all_reduce unit of iris_concurrent,
+ *   comm_chunk        elements per flat unit (the collectives of
+ *                     iris_concurrent, the peer blocks of iris_mm_ag_local),
  *                     multiple of 2048. Default 65536.
- *   mode              IRIS_MODE_FUSED (default) or IRIS_MODE_SEQUENTIAL.
+ *   mode              IRIS_MODE_FUSED (default), IRIS_MODE_SEQUENTIAL or
+ *                     IRIS_MODE_TWO_STREAM.
  *   flags             IRIS_FLAG_* bits.
  */
 typedef struct iris_config {
@@ -173,17 +189,43 @@ int iris_mm_ar_local(void* out, void* C, const void* A, const void* B,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Independent GEMM beside a collective ([PR544]):
- *   C = A @ B + bias                                (M, N), and independently
- *   comm_out[i] = sum_{w<W} comm_in[w][i]           (all_reduce, comm_elems)
- * collective must be IRIS_COLL_ALL_REDUCE (others: IRIS_ERR_UNSUPPORTED).
- * comm_in: host array of W device pointers, each comm_elems fp16;
- * comm_elems % 8 == 0.
+ * matmul_all_gather, local share ([DOCS] matmul_all_gather):
+ *   out (M*W, N) = all_gather along M of every rank's A @ B + bias
+ * This rank's block, rows [rank*M, (rank+1)*M), is computed here (the GEMM
+ * writes it in place); the other W-1 blocks are copied from peer_blocks: a
+ * host array of W-1 device pointers, each (M, N) fp16, standing in for the
+ * other ranks' results, in rank order with this rank left out. The copies
+ * do not depend on this rank's GEMM. A bias along M has M entries (rows of
+ * this rank's block).
+ */
+int iris_mm_ag_local(void* out, const void* A, const void* B, const void* bias,
+                     const void* const* peer_blocks, int32_t W, int32_t rank,
+                     int64_t M, int64_t N, int64_t K, const iris_config_t* cfg,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Independent GEMM beside a collective ([PR544]), local share of rank
+ * `rank` of W:
+ *   C = A @ B + bias                                    (M, N), and
+ * independently, with comm_in a host array of W device pointers (every
+ * rank's buffer of n = comm_elems fp16 in rank order, this rank's own
+ * included):
+ *   IRIS_COLL_ALL_REDUCE      comm_out[i] = sum_w comm_in[w][i]          (n)
+ *   IRIS_COLL_ALL_GATHER      comm_out[w*n + i] = comm_in[w][i]        (W*n)
+ *   IRIS_COLL_REDUCE_SCATTER  comm_out[i] = sum_w comm_in[w][rank*n/W + i]
+ *                                                                      (n/W)
+ *   IRIS_COLL_ALL_TO_ALL      comm_out[j*n/W + i] = comm_in[j][rank*n/W + i]
+ *                                                                        (n)
+ *   IRIS_COLL_BROADCAST       comm_out[i] = comm_in[rank][i], rank being the
+ *                             root                                       (n)
+ * Sums run in fp32 in rank order and round once to fp16; the others are bit
+ * copies. n % 8 == 0; for reduce_scatter and all_to_all also n % (8 W) == 0.
+ * 0 <= rank < W (ignored by all_reduce and all_gather).
  */
 int iris_concurrent(void* C, const void* A, const void* B, const void* bias,
                     int64_t M, int64_t N, int64_t K, int32_t collective,
-                    void* comm_out, const void* const* comm_in, int32_t W,
-                    int64_t comm_elems, const iris_config_t* cfg,
+                    int32_t rank, void* comm_out, const void* const* comm_in,
+                    int32_t W, int64_t comm_elems, const iris_config_t* cfg,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace an op needs (0 on invalid arguments). The
@@ -214,11 +256,12 @@ int iris_grid_size(int32_t op, const iris_config_t* cfg);
 typedef struct iris_op_args {
   int32_t op;             /* IRIS_OP_* */
   void* C;
-  void* out;              /* A_gathered (AG), out (RS/AR), comm_out (concurrent) */
-  const void* A;          /* A (RS/AR/concurrent); unused for AG */
-  const void* const* srcs;/* A_shards (AG), partials (RS/AR), comm_in */
+  void* out;              /* A_gathered (AG), out (RS/AR/MM_AG), comm_out (concurrent) */
+  const void* A;          /* A (RS/AR/MM_AG/concurrent); unused for AG */
+  const void* const* srcs;/* A_shards (AG), partials (RS/AR), peer_blocks (MM_AG), comm_in */
   int32_t W;
-  int32_t rank;           /* RS only */
+  int32_t rank;           /* RS, MM_AG, and the concurrent collectives */
+  int32_t collective;     /* IRIS_OP_CONCURRENT only */
   const void* B;
   const void* bias;
   int64_t M, N, K;        /* K is K_local for AG */
@@ -258,7 +301,8 @@ int iris_device_info(int32_t device, iris_device_info_t* info);
 const char* iris_status_str(int32_t status);
 /* Message for the last error on this thread ("" if none). */
 const char* iris_last_error_message(void);
-/* Frees the library's own workspaces. */
+/* Frees the library's own workspaces and the stream and events of the
+ * two-stream mode. */
 int iris_finalize(void);
 
 #ifdef __cplusplus

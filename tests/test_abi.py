@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_header_declares_the_four_ops():
     names = declared_functions()
-    for op in ("iris_ag_mm", "iris_mm_rs_local", "iris_mm_ar_local", "iris_concurrent"):
+    for op in ("iris_ag_mm", "iris_mm_rs_local", "iris_mm_ar_local", "iris_concurrent", "iris_mm_ag_local"):
         assert op in names
 
 
@@ -96,10 +96,27 @@ def test_rs_ar_concurrent_argument_errors(lib):
     # N/W not a multiple of 8
     assert lib.iris_mm_rs_local(P, P, P, P, None, ptrs(3), 4, 0, 64, 48, 64, None, None, 0, None) == 4
     assert lib.iris_mm_ar_local(P, None, P, P, None, ptrs(1), 2, 64, 64, 64, None, None, 0, None) == 1
-    # unsupported collective
-    assert lib.iris_concurrent(P, P, P, None, 64, 64, 64, 2, P, ptrs(2), 2, 1024, None, None, 0, None) == 2
+    # unknown collective
+    assert lib.iris_concurrent(P, P, P, None, 64, 64, 64, 6, 0, P, ptrs(2), 2, 1024, None, None, 0, None) == 2
     # comm_elems % 8
-    assert lib.iris_concurrent(P, P, P, None, 64, 64, 64, 1, P, ptrs(2), 2, 1001, None, None, 0, None) == 4
+    assert lib.iris_concurrent(P, P, P, None, 64, 64, 64, 1, 0, P, ptrs(2), 2, 1001, None, None, 0, None) == 4
+    # reduce_scatter / all_to_all: comm_elems % (8 W); rank range for the ranked collectives
+    assert lib.iris_concurrent(P, P, P, None, 64, 64, 64, 3, 0, P, ptrs(4), 4, 1040, None, None, 0, None) == 4
+    assert lib.iris_concurrent(P, P, P, None, 64, 64, 64, 4, 0, P, ptrs(4), 4, 1040, None, None, 0, None) == 4
+    assert lib.iris_concurrent(P, P, P, None, 64, 64, 64, 5, 2, P, ptrs(2), 2, 1024, None, None, 0, None) == 1
+    assert lib.iris_concurrent(P, P, P, None, 64, 64, 64, 3, -1, P, ptrs(2), 2, 1024, None, None, 0, None) == 1
+    # matmul_all_gather: rank range, peer pointers
+    assert lib.iris_mm_ag_local(P, P, P, None, ptrs(2), 3, 3, 64, 64, 64, None, None, 0, None) == 1
+    assert lib.iris_mm_ag_local(P, P, P, None, ptrs(2, MIS), 3, 0, 64, 64, 64, None, None, 0, None) == 4
+
+
+def test_two_stream_mode_only_for_independent_ops(lib):
+    from gemm_collective_tile_amd import IRIS_MODE_TWO_STREAM, Config
+    c = ctypes.pointer(Config(mode=IRIS_MODE_TWO_STREAM)._c())
+    # the all_gather feeds the GEMM: refused before any device call
+    assert lib.iris_ag_mm(P, P, ptrs(2), 2, P, None, 256, 256, 256, c, None, 0, None) == 3
+    assert b"two-stream" in lib.iris_last_error_message()
+    assert lib.iris_mm_rs_local(P, P, P, P, None, ptrs(1), 2, 0, 64, 64, 64, c, None, 0, None) == 3
 
 
 def test_config_errors_before_any_device_call(lib):
