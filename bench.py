@@ -156,11 +156,13 @@ def measure(name, steps, warmup, sweep, fixed_wgs=0):
     w = case.w
     Config = il.Config
     best = fixed_wgs or None
-    sweep_ms = {}
+    sweep_ms, pred_ms, pred_best = {}, {}, None
     if sweep and not fixed_wgs:
         cands = case.sweep_candidates()
         log(f"[{name}] sweeping gemm_wgs over {cands}")
         best, sweep_ms = il.iris_tune_gemm_wgs(case.op, cands, reps=5, **case.tune_kw)
+        shape = {k: v for k, v in case.tune_kw.items() if k in ("W", "rank", "M", "N", "K", "comm_elems")}
+        pred_best, pred_ms = il.iris_predict_gemm_wgs(case.op, cands, case.G_wgs, **shape)
     cfg = Config(gemm_wgs=best or 0)
     log(f"[{name}] timing fused mode, gemm_wgs={best}")
     wall_ms, mean_ms = time_steps(case, cfg, steps, warmup)
@@ -171,11 +173,23 @@ def measure(name, steps, warmup, sweep, fixed_wgs=0):
     seq_wall, seq_mean = time_steps(case, seq_cfg, max(3, steps // 2), 2)
     case.step(seq_cfg)
     sgwin, scwin = windows(case)
+    two = None
+    if w.op == "concurrent":
+        # the independent GEMM + collective also runs as two kernels on two
+        # streams; best of a few splits
+        two = {}
+        G = case.G_wgs
+        for gw in sorted({best or (G * 7) // 8, (G * 3) // 4, (G * 7) // 8, (G * 15) // 16}):
+            log(f"[{name}] timing two-stream mode, gemm_wgs={gw}")
+            two[gw] = round(time_steps(case, Config(mode=il.IRIS_MODE_TWO_STREAM, gemm_wgs=gw),
+                                       max(3, steps // 2), 2)[0], 4)
     flops = w.gemm_flops
     res = {
         "workload": name, "op": w.op, "M": w.M, "N": w.N, "K": w.K, "W": w.W,
         "gemm_wgs": best, "grid": case.G_wgs, "tile": "256x256x64",
         "sweep_ms": {str(k): round(v, 4) for k, v in sweep_ms.items()},
+        "predicted_ms": {str(k): round(v, 4) for k, v in pred_ms.items()},
+        "predicted_best": pred_best,
         "fused_ms": round(wall_ms, 4), "kernel_ms": round(mean_ms, 4),
         "tflops": round(flops / (wall_ms * 1e-3) / 1e12, 2),
         "kernel_tflops": round(flops / (mean_ms * 1e-3) / 1e12, 2),
@@ -190,6 +204,9 @@ def measure(name, steps, warmup, sweep, fixed_wgs=0):
         "seq_comm_only_gbps": round(w.comm_bytes / (scwin * 1e-3) / 1e9, 1) if scwin else None,
         "fused_le_sequential": wall_ms <= seq_wall,
     }
+    if two:
+        res["two_stream_ms"] = two
+        res["two_stream_best_ms"] = min(two.values())
     res["mfma_frac"] = round(res["kernel_tflops"] / PEAK_FP16_TFLOPS, 4)
     if res["comm_gbps"]:
         res["comm_hbm_frac"] = round(res["comm_gbps"] / PEAK_HBM_GBPS, 4)

@@ -91,6 +91,11 @@ class _OpArgs(ctypes.Structure):
     ]
 
 
+class _PredictParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_double) for n in (
+        "gemm_tflops_per_cu", "tile_overhead_us", "comm_gbps_per_cu", "comm_gbps_chip", "unit_overhead_us")]
+
+
 class _DeviceInfo(ctypes.Structure):
     _fields_ = [("device", ctypes.c_int32), ("compute_units", ctypes.c_int32),
                 ("clock_khz", ctypes.c_int32), ("memory_clock_khz", ctypes.c_int32),
@@ -113,8 +118,11 @@ def _load() -> ctypes.CDLL:
         "iris_concurrent": [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vpp, i32, i64, cfgp, vp, sz, vp],
         "iris_mm_ag_local": [vp, vp, vp, vp, vpp, i32, i32, i64, i64, i64, cfgp, vp, sz, vp],
         "iris_grid_size": [ctypes.c_int32, cfgp],
-        "iris_tune_gemm_wgs": [ctypes.POINTER(_OpArgs), ctypes.POINTER(i32), i32, i32,
+        "iris_tune_gemm_wgs": [ctypes.POINTER(_OpArgs), ctypes.POINTER(i32), i32, i32, i32,
                                ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float), vp],
+        "iris_predict_gemm_wgs": [ctypes.POINTER(_OpArgs), i32, ctypes.POINTER(i32), i32,
+                                  ctypes.POINTER(_PredictParams), ctypes.POINTER(ctypes.c_float),
+                                  ctypes.POINTER(i32)],
         "iris_last_windows": [vp, vp] + [ctypes.POINTER(ctypes.c_double)] * 4,
         "iris_device_info": [i32, ctypes.POINTER(_DeviceInfo)],
         "iris_status_str": [i32],
@@ -278,10 +286,8 @@ def iris_grid_size(config=None, op=IRIS_OP_AG_MM) -> int:
     return g
 
 
-def iris_tune_gemm_wgs(op, candidates, reps=5, config=None, stream=None, *, C=None, out=None, A=None,
-                       srcs=(), W=1, rank=0, collective=0, B=None, bias=None, M=0, N=0, K=0, comm_elems=0):
-    """Sweep gemm_wgs over `candidates` (the static default is always added),
-    cache and return (best, {candidate: median ms})."""
+def _op_args(op, config, C=None, out=None, A=None, srcs=(), W=1, rank=0, collective=0, B=None, bias=None,
+             M=0, N=0, K=0, comm_elems=0):
     keep = _ptr_array(list(srcs), "srcs")
     a = _OpArgs()
     a.op = op
@@ -294,11 +300,43 @@ def iris_tune_gemm_wgs(op, candidates, reps=5, config=None, stream=None, *, C=No
     a.bias = _ptr(bias, "bias", True)
     a.M, a.N, a.K, a.comm_elems = M, N, K, comm_elems
     a.cfg = (config if isinstance(config, Config) else Config(**(config or {})))._c()
+    return a, keep
+
+
+def iris_tune_gemm_wgs(op, candidates, reps=5, config=None, stream=None, *, top_k=0, C=None, out=None, A=None,
+                       srcs=(), W=1, rank=0, collective=0, B=None, bias=None, M=0, N=0, K=0, comm_elems=0):
+    """Sweep gemm_wgs over `candidates` (the static default is always added),
+    cache and return (best, {candidate: median ms}). With top_k > 0 only the
+    top_k candidates the predictor ranks best are run (the others read -1)."""
+    a, keep = _op_args(op, config, C, out, A, srcs, W, rank, collective, B, bias, M, N, K, comm_elems)
     cands = (ctypes.c_int32 * max(1, len(candidates)))(*candidates)
     ms = (ctypes.c_float * max(1, len(candidates)))()
     best = ctypes.c_int32(0)
-    _check(_lib.iris_tune_gemm_wgs(ctypes.byref(a), cands, len(candidates), reps, ctypes.byref(best),
+    _check(_lib.iris_tune_gemm_wgs(ctypes.byref(a), cands, len(candidates), reps, top_k, ctypes.byref(best),
                                    ms, _stream(stream)))
+    del keep
+    return best.value, {c: ms[i] for i, c in enumerate(candidates)}
+
+
+def iris_predict_gemm_wgs(op, candidates, grid, config=None, params=None, *, W=1, rank=0, collective=0,
+                          M=0, N=0, K=0, comm_elems=0):
+    """Predicted makespan (ms) of the fused schedule for each gemm_wgs
+    candidate on a grid of `grid` workgroups; returns (best, {candidate: ms}).
+    Host only: needs the shapes, no tensors. `params` is a dict of the
+    model's rates (gemm_tflops_per_cu, tile_overhead_us, comm_gbps_per_cu,
+    comm_gbps_chip, unit_overhead_us); missing ones take the defaults."""
+    a, keep = _op_args(op, config, W=W, rank=rank, collective=collective, M=M, N=N, K=K, comm_elems=comm_elems)
+    pp = _PredictParams(*[-1.0] * 5)
+    for k, v in (params or {}).items():
+        if k not in dict(_PredictParams._fields_):
+            raise ValueError(f"unknown predictor parameter {k!r}")
+        setattr(pp, k, float(v))
+    cands = (ctypes.c_int32 * max(1, len(candidates)))(*candidates)
+    ms = (ctypes.c_float * max(1, len(candidates)))()
+    best = ctypes.c_int32(0)
+    _check(_lib.iris_predict_gemm_wgs(ctypes.byref(a), grid, cands, len(candidates), ctypes.byref(pp), ms,
+                                      ctypes.byref(best)))
+    del keep
     return best.value, {c: ms[i] for i, c in enumerate(candidates)}
 
 

@@ -153,6 +153,32 @@ void save_cache_entry(const std::string& key, int value) {
   if (!ok || rename(tmp.c_str(), path.c_str()) != 0) unlink(tmp.c_str());
 }
 
+// The cache file is read once per path and process; later tunings in this
+// process update the in-memory copy, so an op call costs no file access.
+std::mutex g_cache_mu;
+std::string g_cache_path;
+std::map<std::string, int> g_cache;
+bool g_cache_loaded = false;
+
+int tuned_gemm_wgs(const std::string& key) {
+  std::lock_guard<std::mutex> lk(g_cache_mu);
+  const std::string path = cache_path();
+  if (!g_cache_loaded || path != g_cache_path) {
+    g_cache = load_cache();
+    g_cache_path = path;
+    g_cache_loaded = true;
+  }
+  auto it = g_cache.find(key);
+  return it == g_cache.end() ? 0 : it->second;
+}
+
+void remember_gemm_wgs(const std::string& key, int value) {
+  std::lock_guard<std::mutex> lk(g_cache_mu);
+  save_cache_entry(key, value);
+  const std::string path = cache_path();
+  if (g_cache_loaded && path == g_cache_path) g_cache[key] = value;
+}
+
 // --------------------------------------------------------------- config
 struct Resolved {
   int bm, bn, bk, gm, gemm_wgs, comm_bm, comm_bn, comm_chunk, mode, flags;
@@ -212,12 +238,7 @@ int resolve_device(Resolved* r, int kind, const DevInfo& di, const std::string& 
   r->grid = di.cus * occ;
   if (r->grid > 2048) r->grid = 2048;
   if (r->gemm_wgs <= 0) {
-    int tuned = 0;
-    if (r->mode == IRIS_MODE_FUSED) {
-      std::map<std::string, int> db = load_cache();
-      auto it = db.find(key);
-      if (it != db.end()) tuned = it->second;
-    }
+    const int tuned = r->mode == IRIS_MODE_FUSED ? tuned_gemm_wgs(key) : 0;
     r->gemm_wgs = (tuned > 0 && tuned < r->grid) ? tuned : (r->grid * 7) / 8;
   }
   if (r->mode != IRIS_MODE_SEQUENTIAL && (r->gemm_wgs < 1 || r->gemm_wgs > r->grid - 1))
@@ -590,6 +611,15 @@ int copy_ptrs(const void* const* arr, int n, const char* name) {
 }  // namespace
 
 // ====================================================================== ABI
+namespace iris {
+// Records the message for iris_last_error_message from the library's other
+// translation units; returns status.
+int set_error(int status, const char* msg) {
+  g_msg = msg;
+  return status;
+}
+}  // namespace iris
+
 extern "C" {
 
 int iris_ag_mm(void* C, void* A_gathered, const void* const* A_shards, int32_t W, const void* B,
@@ -809,7 +839,7 @@ int iris_grid_size(int32_t op, const iris_config_t* cfg) {
 }
 
 int iris_tune_gemm_wgs(const iris_op_args_t* a, const int32_t* candidates, int32_t n_candidates, int32_t reps,
-                       int32_t* best_gemm_wgs, float* ms_out, void* stream) {
+                       int32_t top_k, int32_t* best_gemm_wgs, float* ms_out, void* stream) {
   g_msg.clear();
   if (!a || !best_gemm_wgs) return fail(IRIS_ERR_INVALID_ARG, "args and best_gemm_wgs must not be NULL");
   if (n_candidates < 0 || (n_candidates > 0 && !candidates))
@@ -821,6 +851,20 @@ int iris_tune_gemm_wgs(const iris_op_args_t* a, const int32_t* candidates, int32
   int G = iris_grid_size(a->op, &cfg);
   if (G < 0) return -G;
   std::vector<int> cands(candidates, candidates + n_candidates);
+  std::vector<int> bench_idx;  // position in `candidates` of each benchmarked candidate
+  for (int i = 0; i < n_candidates; ++i) bench_idx.push_back(i);
+  if (top_k > 0 && top_k < n_candidates) {
+    std::vector<float> pred((size_t)n_candidates);
+    const int ps = iris_predict_gemm_wgs(a, G, candidates, n_candidates, nullptr, pred.data(), nullptr);
+    if (ps) return fail(ps, "the split predictor rejected the op or a candidate");
+    std::stable_sort(bench_idx.begin(), bench_idx.end(), [&](int x, int y) { return pred[x] < pred[y]; });
+    bench_idx.resize(top_k);
+    std::sort(bench_idx.begin(), bench_idx.end());
+    cands.clear();
+    for (int i : bench_idx) cands.push_back(candidates[i]);
+    if (ms_out)
+      for (int i = 0; i < n_candidates; ++i) ms_out[i] = -1.0f;
+  }
   const int def = (G * 7) / 8;
   if (std::find(cands.begin(), cands.end(), def) == cands.end()) cands.push_back(def);
   auto call = [&](int gw) -> int {
@@ -879,7 +923,7 @@ int iris_tune_gemm_wgs(const iris_op_args_t* a, const int32_t* candidates, int32
     if (status) break;
     std::sort(t.begin(), t.end());
     const float med = t[t.size() / 2];
-    if (ms_out && (int)i < n_candidates) ms_out[i] = med;
+    if (ms_out && i < bench_idx.size()) ms_out[bench_idx[i]] = med;
     if (best < 0 || med < best_ms || (med == best_ms && gw > best)) {
       best = gw;
       best_ms = med;
@@ -896,7 +940,7 @@ int iris_tune_gemm_wgs(const iris_op_args_t* a, const int32_t* candidates, int32
     resolve_static(&cfg, &r);
     // AG keys on K_local (args->K), the other ops on K, as run() looks them up
     const int coll = a->op == IRIS_OP_CONCURRENT ? (a->collective > 0 ? a->collective : IRIS_COLL_ALL_REDUCE) : 0;
-    save_cache_entry(cache_key(di.arch, a->op * 16 + coll, a->M, a->N, a->K, a->W, r.bm, r.bn, r.bk, r.gm), best);
+    remember_gemm_wgs(cache_key(di.arch, a->op * 16 + coll, a->M, a->N, a->K, a->W, r.bm, r.bn, r.bk, r.gm), best);
   }
   return IRIS_OK;
 }

@@ -250,8 +250,12 @@ int iris_grid_size(int32_t op, const iris_config_t* cfg);
  * of each candidate to ms_out[i] (may be NULL), and stores the winner in the
  * tuning cache (file named by IRIS_LOCAL_TUNE_CACHE, default
  * ~/.cache/iris_local/tune.txt; written to a temporary file then renamed;
- * a failed write is ignored). Blocks until done. Ties go to more GEMM
+ * a failed write is ignored; the file is read once per process, and this
+ * process's later tunings update that copy). Blocks until done. Ties go to more GEMM
  * workgroups. The op's outputs hold the last candidate's results.
+ * top_k > 0 (and below n_candidates): rank the candidates with
+ * iris_predict_gemm_wgs first and benchmark only the top_k best predicted
+ * (plus the default); ms_out of a candidate left out is -1.
  */
 typedef struct iris_op_args {
   int32_t op;             /* IRIS_OP_* */
@@ -270,8 +274,36 @@ typedef struct iris_op_args {
 } iris_op_args_t;
 
 int iris_tune_gemm_wgs(const iris_op_args_t* args, const int32_t* candidates,
-                       int32_t n_candidates, int32_t reps, int32_t* best_gemm_wgs,
-                       float* ms_out, void* stream);
+                       int32_t n_candidates, int32_t reps, int32_t top_k,
+                       int32_t* best_gemm_wgs, float* ms_out, void* stream);
+
+/*
+ * Analytical CU split ([PR544]: predictor, a work-stealing makespan
+ * simulation used to rank splits before benchmarking the top k). Replays
+ * the fused schedule of the op in `args` on a grid of `grid` workgroups for
+ * each candidate gemm_wgs (1 .. grid-1) with modelled durations, writes the
+ * predicted milliseconds to predicted_ms[i] (may be NULL) and the best
+ * candidate to *best_gemm_wgs (ties to more GEMM workgroups). Host code
+ * only: no device call and no workspace; errors set iris_last_error_message.
+ * params may be NULL (a rate <= 0 or an overhead < 0 means its default); the
+ * defaults were measured on MI355X:
+ *   gemm_tflops_per_cu  sustained GEMM rate of one CU          4.4
+ *   tile_overhead_us    fixed cost per GEMM tile                2
+ *   comm_gbps_per_cu    copy/reduce rate of one workgroup       45
+ *   comm_gbps_chip      comm bandwidth of the whole chip        5200
+ *   unit_overhead_us    fixed cost per comm unit                1
+ */
+typedef struct iris_predict_params {
+  double gemm_tflops_per_cu;
+  double tile_overhead_us;
+  double comm_gbps_per_cu;
+  double comm_gbps_chip;
+  double unit_overhead_us;
+} iris_predict_params_t;
+
+int iris_predict_gemm_wgs(const iris_op_args_t* args, int32_t grid, const int32_t* candidates,
+                          int32_t n_candidates, const iris_predict_params_t* params,
+                          float* predicted_ms, int32_t* best_gemm_wgs);
 
 /*
  * Windows of the last op that used `workspace` (or the library's own

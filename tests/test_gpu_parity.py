@@ -335,3 +335,34 @@ def test_workspace_shared_across_layouts():
                                 config=Config(block_m=tile[0], block_n=tile[1], comm_block_n=64))
             torch.cuda.synchronize()
             assert_close(out, ref, f"out tile={tile} fill={fill}")
+
+
+def test_tune_gemm_wgs_and_top_k(tmp_path, monkeypatch):
+    """The split sweep benchmarks every candidate (or, with top_k, only the
+    best predicted ones, the rest reading -1), returns a benchmarked winner
+    that is then used by default, and leaves outputs equal to the oracle's."""
+    monkeypatch.setenv("IRIS_LOCAL_TUNE_CACHE", str(tmp_path / "tune.txt"))
+    W, M, N, kl = 4, 1024, 1024, 256
+    inp = ag_inputs(M, N, kl, W, seed=21)
+    shards, B, bias = cuda(inp["shards"]), cuda(inp["B"]), cuda(inp["bias"])
+    G = il.iris_grid_size(None, il.IRIS_OP_AG_MM)
+    cands = sorted({max(1, G // 8), G // 4, G // 2, (3 * G) // 4, G - 1})
+    Gref, Cref = oracle_ag(inp)
+    for top_k in (0, 2):
+        note(f"tune ag_mm top_k={top_k} candidates={cands}")
+        C, Gb = empty((M, N)), empty((M, kl * W))
+        best, ms = il.iris_tune_gemm_wgs(il.IRIS_OP_AG_MM, cands, reps=3, top_k=top_k, C=C, out=Gb, srcs=shards,
+                                         W=W, B=B, bias=bias, M=M, N=N, K=kl)
+        torch.cuda.synchronize()
+        ran = [c for c in cands if ms[c] >= 0]
+        assert len(ran) == (len(cands) if top_k == 0 else top_k)
+        assert all(ms[c] > 0 for c in ran)
+        if top_k:
+            _, pred = il.iris_predict_gemm_wgs(il.IRIS_OP_AG_MM, cands, G, W=W, M=M, N=N, K=kl)
+            order = sorted(cands, key=lambda c: (pred[c], cands.index(c)))
+            assert sorted(ran) == sorted(order[:top_k])
+        assert best in ran or best == (G * 7) // 8
+        assert_bits_equal(Gb, Gref, f"gathered after tuning top_k={top_k}")
+        assert_close(C, Cref, f"C after tuning top_k={top_k}")
+        C2, G2 = run_ag(inp)  # uses the tuned split from the cache
+        assert_bits_equal(C2, C, f"tuned default top_k={top_k}")

@@ -1,0 +1,152 @@
+"""The analytical CU-split predictor (host code, no GPU).
+
+Each expected makespan below is worked out by hand from the scheduling rules
+the predictor replays (workgroups below gemm_wgs start on the GEMM queue, the
+rest on the comm queue, each switches queues once; an all_gather_matmul tile
+waits for the copy units of its row block and takes copy units meanwhile; a
+reduce unit waits for the tiles of its columns), with a rate model chosen so
+the durations are round numbers:
+
+    GEMM tile  = 2*rows*cols*K / (1 TFLOP/s)          (no fixed cost)
+    comm unit  = bytes / (1 GB/s per workgroup)       (no fixed cost)
+
+and a chip-wide comm ceiling far above the per-workgroup rate unless a test
+says otherwise.
+"""
+import pytest
+
+import gemm_collective_tile_amd as il
+from gemm_collective_tile_amd import Config, IrisError
+
+UNIT = dict(gemm_tflops_per_cu=1.0, tile_overhead_us=0.0, comm_gbps_per_cu=1.0, comm_gbps_chip=1e9,
+            unit_overhead_us=0.0)
+
+
+def tile_ms(rows, cols, K):
+    return 2.0 * rows * cols * K / 1e12 * 1e3
+
+
+def unit_ms(nbytes, gbps=1.0):
+    return nbytes / (gbps * 1e9) * 1e3
+
+
+def predict(op, cands, grid, config=None, params=UNIT, **shape):
+    return il.iris_predict_gemm_wgs(op, cands, grid, config=config, params=params, **shape)
+
+
+def test_independent_one_tile_one_unit():
+    # concurrent broadcast: 1 tile beside 1 copy unit of 2048 elements (4 bytes each: read + write)
+    best, ms = predict(il.IRIS_OP_CONCURRENT, [1], 2, Config(comm_chunk=2048), W=2, collective=il.IRIS_COLL_BROADCAST,
+                       M=256, N=256, K=1024, comm_elems=2048)
+    assert best == 1
+    assert ms[1] == pytest.approx(max(tile_ms(256, 256, 1024), unit_ms(2048 * 4)), rel=1e-6)
+
+
+def test_comm_workgroup_steals_gemm_tiles():
+    # 8 tiles, 4 workgroups, 3 on GEMM; the comm one finishes its unit and takes tiles 3 and 7
+    t, u = tile_ms(256, 256, 1024), unit_ms(2048 * 4)
+    shape = dict(W=2, collective=il.IRIS_COLL_BROADCAST, M=512, N=1024, K=1024, comm_elems=2048)
+    _, ms = predict(il.IRIS_OP_CONCURRENT, [3], 4, Config(comm_chunk=2048), **shape)
+    assert ms[3] == pytest.approx(u + 2 * t, rel=1e-6)
+    # without stealing the 3 GEMM workgroups take the 8 tiles in 3 rounds
+    _, ms = predict(il.IRIS_OP_CONCURRENT, [3], 4, Config(comm_chunk=2048, flags=il.IRIS_FLAG_NO_STEAL), **shape)
+    assert ms[3] == pytest.approx(3 * t, rel=1e-6)
+
+
+def test_all_gather_tile_waits_for_its_row_block():
+    # W=2, one 256x256 tile over K = 2*256; two copy units of 256 rows x 256 cols (read + write 2 bytes each).
+    # The GEMM workgroup holds the tile and copies one unit while the other copies the second.
+    _, ms = predict(il.IRIS_OP_AG_MM, [1], 2, Config(comm_block_m=256), W=2, M=256, N=256, K=256)
+    assert ms[1] == pytest.approx(unit_ms(256 * 256 * 4) + tile_ms(256, 256, 512), rel=1e-6)
+
+
+def test_reduce_scatter_units_wait_for_their_tiles():
+    # W=2, rank 0: the slice is columns 0..255, tile (0,0) comes first; 4 reduce units of 64 rows x 256
+    # columns (W reads + 1 write of 2 bytes) all need tile (0,0). Workgroup 1 waits for it, then reduces
+    # units 0, 1, 3; workgroup 0 does tile 1, then unit 2.
+    t, u = tile_ms(256, 256, 1024), unit_ms(64 * 256 * 2 * 3)
+    _, ms = predict(il.IRIS_OP_MM_RS, [1], 2, W=2, rank=0, M=256, N=512, K=1024)
+    assert ms[1] == pytest.approx(t + 3 * u, rel=1e-6)
+
+
+def test_chip_ceiling_bounds_the_comm_time():
+    # 64 copy units of 64 KiB elements on 64 comm workgroups; the chip ceiling of 4 GB/s binds.
+    p = dict(UNIT, comm_gbps_chip=4.0)
+    n = 64 * 65536
+    _, ms = predict(il.IRIS_OP_CONCURRENT, [1], 65, params=p, W=2, collective=il.IRIS_COLL_BROADCAST,
+                    M=256, N=256, K=64, comm_elems=n)
+    assert ms[1] >= unit_ms(n * 4, 4.0) * (1 - 1e-6)
+
+
+@pytest.mark.parametrize("op,extra", [
+    (il.IRIS_OP_AG_MM, dict(W=8, M=4096, N=4096, K=512)),
+    (il.IRIS_OP_MM_RS, dict(W=8, rank=3, M=8192, N=8192, K=2048)),
+    (il.IRIS_OP_MM_AR, dict(W=4, M=4096, N=4096, K=4096)),
+    (il.IRIS_OP_CONCURRENT, dict(W=8, collective=il.IRIS_COLL_ALL_REDUCE, M=8192, N=8192, K=8192,
+                                 comm_elems=64 << 20)),
+    (il.IRIS_OP_MM_AG, dict(W=8, rank=2, M=4096, N=4096, K=4096)),
+])
+def test_lower_bounds_with_default_rates(op, extra):
+    """The makespan is at least the GEMM work over the whole grid at the
+    modelled rate, and the best prediction is one of the candidates."""
+    grid = 256
+    cands = [16, 64, 128, 192, 224, 255]
+    best, ms = il.iris_predict_gemm_wgs(op, cands, grid, **extra)
+    assert best in cands and ms[best] == min(ms.values())
+    M, N = extra["M"], extra["N"]
+    K = extra["K"] * (extra["W"] if op == il.IRIS_OP_AG_MM else 1)
+    gemm_ms = 2.0 * M * N * K / (4.4e12 * grid) * 1e3
+    for v in ms.values():
+        assert v >= gemm_ms * (1 - 1e-6)
+
+
+def test_without_stealing_the_best_split_balances_the_queues():
+    # GEMM 8192^3 (1024 tiles) beside an all_reduce of 8 x 64Mi elements (1024 units of 65536), with
+    # no queue switching: the makespan is the longer of ceil(1024/g) tiles and ceil(1024/(256-g)) units,
+    # which is smallest at an interior split
+    p = dict(gemm_tflops_per_cu=4.4, tile_overhead_us=2.0, comm_gbps_per_cu=45.0, comm_gbps_chip=5200.0,
+             unit_overhead_us=1.0)
+    t = 2e-3 + tile_ms(256, 256, 8192) / 4.4
+    u = 1e-3 + unit_ms(65536 * 2 * 9, 45.0)
+    cands = [32, 64, 128, 192, 224, 240, 255]
+    best, ms = predict(il.IRIS_OP_CONCURRENT, cands, 256, Config(flags=il.IRIS_FLAG_NO_STEAL), params=p, W=8,
+                       collective=il.IRIS_COLL_ALL_REDUCE, M=8192, N=8192, K=8192, comm_elems=64 << 20)
+    assert best == 224
+    for g in cands:
+        nc = 256 - g
+        if nc <= 115:  # below the chip ceiling every unit runs at the per-workgroup rate
+            expect = max(-(-1024 // g) * t, -(-1024 // nc) * u)
+            assert ms[g] == pytest.approx(expect, rel=1e-5), g
+
+
+def test_ties_go_to_more_gemm_workgroups():
+    # one tile and one unit: every split gives the same makespan
+    best, ms = predict(il.IRIS_OP_CONCURRENT, [1, 2, 3], 4, Config(comm_chunk=2048), W=2,
+                       collective=il.IRIS_COLL_BROADCAST, M=256, N=256, K=1024, comm_elems=2048)
+    assert len(set(ms.values())) == 1
+    assert best == 3
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(op=il.IRIS_OP_AG_MM, cands=[1], grid=1), "grid"),
+    (dict(op=il.IRIS_OP_AG_MM, cands=[0], grid=8), "candidate"),
+    (dict(op=il.IRIS_OP_AG_MM, cands=[8], grid=8), "candidate"),
+    (dict(op=99, cands=[1], grid=8), "unknown op"),
+    (dict(op=il.IRIS_OP_MM_RS, cands=[1], grid=8, N=1000, W=3), "reduce_scatter"),
+    (dict(op=il.IRIS_OP_MM_RS, cands=[1], grid=8, rank=4, W=4), "reduce_scatter"),
+    (dict(op=il.IRIS_OP_CONCURRENT, cands=[1], grid=8, comm_elems=0), "comm_elems"),
+    (dict(op=il.IRIS_OP_CONCURRENT, cands=[1], grid=8, comm_elems=4096, collective=9), "collective"),
+    (dict(op=il.IRIS_OP_AG_MM, cands=[1], grid=8, M=0), "positive"),
+])
+def test_invalid_arguments(kw, msg):
+    shape = dict(W=2, rank=0, M=256, N=1024, K=256)
+    kw = dict(kw)
+    op, cands, grid = kw.pop("op"), kw.pop("cands"), kw.pop("grid")
+    shape.update(kw)
+    with pytest.raises(IrisError, match=msg):
+        il.iris_predict_gemm_wgs(op, cands, grid, **shape)
+
+
+def test_unknown_parameter_name():
+    with pytest.raises(ValueError):
+        il.iris_predict_gemm_wgs(il.IRIS_OP_AG_MM, [1], 8, params={"gemm_rate": 1.0}, W=2, M=256, N=256, K=256)
