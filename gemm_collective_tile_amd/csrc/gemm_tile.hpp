@@ -75,7 +75,10 @@ struct TileShape {
   static constexpr int B_STAGE = BK * RB;
   static constexpr int STAGE = A_STAGE + B_STAGE;
   static constexpr int B_RING = NSTAGE * A_STAGE;     // LDS: [A stages | B stages]
-  static constexpr int LDS_BYTES = NSTAGE * STAGE;
+  static constexpr int STAGES_BYTES = NSTAGE * STAGE;
+  // the tile's bias (BN columns or BM rows of fp16), staged for the epilogue
+  static constexpr int BIAS_OFF = STAGES_BYTES;
+  static constexpr int LDS_BYTES = STAGES_BYTES + 2 * (BM > BN ? BM : BN);
   static constexpr int A_LD = A_STAGE / 16 / 256;     // 16-byte chunks per thread per step
   static constexpr int B_LD = B_STAGE / 16 / 256;
   static_assert(FM >= 1 && FN >= 1, "tile too small for 32x32 blocks");
@@ -113,8 +116,15 @@ struct GemmPipe {
   uint32_t a_off[S::A_LD];
   uint32_t a_kc;             // k offset (elements) of this thread's A chunks
   uint32_t b_off[S::B_LD];
-  uint32_t a_lds[S::A_LD];
-  uint32_t b_lds[S::B_LD];   // includes B_RING
+  // LDS offsets of chunk 0; chunk n lies a fixed distance further (the
+  // swizzles depend on the row only through bits that chunk n's row offset
+  // leaves alone), so the distance folds into the LDS write's immediate
+  uint32_t a_lds0;
+  uint32_t b_lds0;           // includes B_RING
+  static constexpr uint32_t A_ROWS_PER_LD = 256 / S::CPR_A;  // A rows per chunk index
+  static constexpr uint32_t B_ROWS_PER_LD = 256 / S::CPR_B;  // B k rows per chunk index
+  static_assert(A_ROWS_PER_LD % 16 == 0, "A chunk rows must keep the A swizzle");
+  static_assert(B_ROWS_PER_LD % 4 == 0, "B chunk rows must keep the B swizzle");
   // LDS byte offsets of the fragment reads within the A / B rings
   uint32_t ra_base[S::NSL];   // A, per k slice
   uint32_t rb_base[S::FN];    // B, per 32-column block (includes B_RING)
@@ -131,8 +141,8 @@ struct GemmPipe {
     for (int n = 0; n < S::A_LD; ++n) {
       const uint32_t r = (tid + 256 * n) / S::CPR_A;
       a_off[n] = (uint32_t)((r * g.lda + 8 * ca) * 2);
-      a_lds[n] = r * S::RA + ((ca ^ swz_a(r)) << 4);
     }
+    a_lds0 = (tid / S::CPR_A) * S::RA + ((ca ^ swz_a(tid / S::CPR_A)) << 4);
     // B chunk c = tid + 256 n: k row c / CPR_B, column chunk c % CPR_B
 #pragma unroll
     for (int n = 0; n < S::B_LD; ++n) {
@@ -140,7 +150,10 @@ struct GemmPipe {
       const uint32_t k = c / S::CPR_B, ch = c % S::CPR_B;
       const bool ok = n0 + 8 * (int)ch < g.N;
       b_off[n] = ok ? (uint32_t)((k * g.ldb + 8 * ch) * 2) : kOob;
-      b_lds[n] = S::B_RING + k * S::RB + ((ch ^ swz_b<S>(k)) << 4);
+    }
+    {
+      const uint32_t k = tid / S::CPR_B, ch = tid % S::CPR_B;
+      b_lds0 = S::B_RING + k * S::RB + ((ch ^ swz_b<S>(k)) << 4);
     }
     {
       const uint32_t r = wm * S::WTM + (l & 31);
@@ -195,9 +208,9 @@ struct GemmPipe {
   template <int D>
   __device__ __forceinline__ void store(char* lds, int ST, const Regs& R) const {
     if constexpr (D < S::A_LD)
-      *(u32x4*)(lds + ST * S::A_STAGE + a_lds[D]) = R.v[D];
+      *(u32x4*)(lds + a_lds0 + (ST * S::A_STAGE + D * A_ROWS_PER_LD * S::RA)) = R.v[D];
     else
-      *(u32x4*)(lds + ST * S::B_STAGE + b_lds[D - S::A_LD]) = R.v[D];
+      *(u32x4*)(lds + b_lds0 + (ST * S::B_STAGE + (D - S::A_LD) * B_ROWS_PER_LD * S::RB)) = R.v[D];
   }
 
   struct Frags {
@@ -411,6 +424,12 @@ __device__ __forceinline__ void read_all(const GemmPipe<S>& P, const char* lds, 
 // S::LDS_BYTES. Starts with a workgroup barrier so callers may reuse the LDS
 // before it; the LDS writes of its last step target a stage nobody reads,
 // and the caller's next use of the LDS starts with a barrier.
+// The tile's bias is read from global memory at the start, next to the first
+// operand loads, and parked in LDS; the epilogue takes this lane's bias
+// values from there before it touches the accumulators. With a global bias
+// load next to each store, the epilogue of a 256x256 tile took about 25 us
+// on MI355X (load latency, and the register allocator reading out every
+// accumulator up front and spilling); this way 11-16 us.
 template <class S>
 __device__ void gemm_tile(const GemmArgs& g, int m0, int n0, char* lds) {
   using P_t = GemmPipe<S>;
@@ -433,9 +452,16 @@ __device__ void gemm_tile(const GemmArgs& g, int m0, int n0, char* lds) {
   typename P_t::Frags f0, f1;
   typename P_t::Regs R0, R1;
 
+  const int bias_n = g.bias_along_m ? S::BM : S::BN;
+  f16 bias_v = (f16)0.0f;
+  if (g.bias && (int)threadIdx.x < bias_n) {
+    const int idx = (g.bias_along_m ? m0 : n0) + (int)threadIdx.x;
+    if (idx < (g.bias_along_m ? g.M : g.N)) bias_v = g.bias[idx];
+  }
   load_all<S, 0>(P, P.rsrc(g, m0, n0, 0), R0);
   load_all<S, 0>(P, P.rsrc(g, m0, n0, 1), R1);
   __syncthreads();  // previous users of the LDS are done
+  if (g.bias && (int)threadIdx.x < bias_n) ((f16*)(lds + S::BIAS_OFF))[threadIdx.x] = bias_v;
   store_all<S, 0>(P, lds, 0, R0);
   __syncthreads();
   read_all<S, 0, NR>(P, lds, 0, f0);
@@ -446,6 +472,7 @@ __device__ void gemm_tile(const GemmArgs& g, int m0, int n0, char* lds) {
   // out-of-range zeros and adds exact zeros to accumulators that start at
   // +0, so it changes no bit of the result.
   const int nk2 = (nk + 1) & ~1;
+  __builtin_assume(nk2 >= 2);  // K >= 1: the host rejects K = 0
   for (int t = 0; t < nk2; t += 2) {
     k_step<S, 0>(P, g, m0, n0, t, lds, R0, R1, f0, f1, acc);
     k_step<S, 1>(P, g, m0, n0, t + 1, lds, R1, R0, f0, f1, acc);
@@ -454,11 +481,21 @@ __device__ void gemm_tile(const GemmArgs& g, int m0, int n0, char* lds) {
   // epilogue: lane holds row m = lane & 31 of each 32x32 block and, for
   // q = 0..3, columns 8q + 4*(lane >> 5) + 0..3.
   const int khalf = lane >> 5;
+  const f16* bias_l = (const f16*)(lds + S::BIAS_OFF);
+  const bool col_bias = g.bias && !g.bias_along_m;
+  const bool row_bias = g.bias && g.bias_along_m;
+  f16x4 bn_v[S::FN][4];
+#pragma unroll
+  for (int j = 0; j < S::FN; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      bn_v[j][q] = col_bias ? *(const f16x4*)(bias_l + wn * S::WTN + j * 32 + 8 * q + 4 * khalf) : f16x4{};
 #pragma unroll
   for (int i = 0; i < S::FM; ++i) {
-    const int m = m0 + wm * S::WTM + i * 32 + (lane & 31);
+    const int r = wm * S::WTM + i * 32 + (lane & 31);
+    const int m = m0 + r;
     if (m >= g.M) continue;
-    const float bm = (g.bias && g.bias_along_m) ? (float)g.bias[m] : 0.0f;
+    const float bm = row_bias ? (float)bias_l[r] : 0.0f;
 #pragma unroll
     for (int j = 0; j < S::FN; ++j) {
 #pragma unroll
@@ -466,10 +503,9 @@ __device__ void gemm_tile(const GemmArgs& g, int m0, int n0, char* lds) {
         const int n = n0 + wn * S::WTN + j * 32 + 8 * q + 4 * khalf;
         if (n >= g.N) continue;
         f16x4 o;
-        if (g.bias && !g.bias_along_m) {
-          const f16x4 bv = *(const f16x4*)(g.bias + n);
+        if (col_bias) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = (f16)(acc[i][j][4 * q + e] + (float)bv[e]);
+          for (int e = 0; e < 4; ++e) o[e] = (f16)(acc[i][j][4 * q + e] + (float)bn_v[j][q][e]);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = (f16)(acc[i][j][4 * q + e] + bm);
