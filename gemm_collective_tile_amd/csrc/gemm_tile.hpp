@@ -478,7 +478,7 @@ __device__ void gemm_tile(const GemmArgs& g, int m0, int n0, char* lds) {
     k_step<S, 1>(P, g, m0, n0, t + 1, lds, R1, R0, f0, f1, acc);
   }
 
-  // epilogue: lane holds row m = lane & 31 of each 32x32 block and, for
+  // epilogue: lane holds row lane & 31 of each 32x32 block and, for
   // q = 0..3, columns 8q + 4*(lane >> 5) + 0..3.
   const int khalf = lane >> 5;
   const f16* bias_l = (const f16*)(lds + S::BIAS_OFF);
@@ -490,18 +490,24 @@ __device__ void gemm_tile(const GemmArgs& g, int m0, int n0, char* lds) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       bn_v[j][q] = col_bias ? *(const f16x4*)(bias_l + wn * S::WTN + j * 32 + 8 * q + 4 * khalf) : f16x4{};
+  // Lanes l and l + 32 hold the two 4-column halves of the same 8 columns
+  // of one row. One permlane32 swap per register pair trades the upper
+  // lanes' q half for the lower lanes' q + 1 half, so that each lane holds 8
+  // consecutive columns (lower lanes 8q.., upper lanes 8q + 8..) and writes
+  // them with one 16-byte store. The swap needs every lane active: values
+  // are computed for all lanes and only the stores are masked.
 #pragma unroll
   for (int i = 0; i < S::FM; ++i) {
     const int r = wm * S::WTM + i * 32 + (lane & 31);
     const int m = m0 + r;
-    if (m >= g.M) continue;
+    const bool m_ok = m < g.M;
     const float bm = row_bias ? (float)bias_l[r] : 0.0f;
+    f16* const crow = g.C + (int64_t)m * g.ldc;
 #pragma unroll
     for (int j = 0; j < S::FN; ++j) {
+      uint32_t w[4][2];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * S::WTN + j * 32 + 8 * q + 4 * khalf;
-        if (n >= g.N) continue;
         f16x4 o;
         if (col_bias) {
 #pragma unroll
@@ -510,7 +516,27 @@ __device__ void gemm_tile(const GemmArgs& g, int m0, int n0, char* lds) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = (f16)(acc[i][j][4 * q + e] + bm);
         }
-        *(f16x4*)(g.C + (int64_t)m * g.ldc + n) = o;
+        const auto u = __builtin_bit_cast(u32x2, o);
+        w[q][0] = u[0];
+        w[q][1] = u[1];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; q += 2) {
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(w[q][d], w[q + 1][d], false, false);
+          w[q][d] = sw[0];
+          w[q + 1][d] = sw[1];
+        }
+        const int n = n0 + wn * S::WTN + j * 32 + 8 * q + 8 * khalf;
+        if (m_ok && n < g.N) {
+          u32x4 v;
+          v[0] = w[q][0];
+          v[1] = w[q][1];
+          v[2] = w[q + 1][0];
+          v[3] = w[q + 1][1];
+          *(u32x4*)(crow + n) = v;
+        }
       }
     }
   }
