@@ -32,8 +32,8 @@ int set_error(int status, const char* msg);  // defined beside the other entry p
 
 namespace iris_predict {
 
-constexpr double kGemmTflopsPerCu = 4.4;   // ~1130 TFLOP/s of 256x256 tiles on 256 CUs
-constexpr double kTileOverheadUs = 2.0;    // prologue (two steps in flight) + epilogue
+constexpr double kGemmTflopsPerCu = 5.0;   // K-loop rate of a 256x256 tile (fit over K = 4096..16384)
+constexpr double kTileOverheadUs = 20.0;   // claim, prologue, epilogue and store drain of a tile
 constexpr double kCommGbpsPerCu = 45.0;    // one 4-wave workgroup copying or reducing
 constexpr double kCommGbpsChip = 5200.0;   // plain copy over the whole chip
 constexpr double kUnitOverheadUs = 1.0;    // claim + release of a comm unit

@@ -287,8 +287,8 @@ int iris_tune_gemm_wgs(const iris_op_args_t* args, const int32_t* candidates,
  * only: no device call and no workspace; errors set iris_last_error_message.
  * params may be NULL (a rate <= 0 or an overhead < 0 means its default); the
  * defaults were measured on MI355X:
- *   gemm_tflops_per_cu  sustained GEMM rate of one CU          4.4
- *   tile_overhead_us    fixed cost per GEMM tile                2
+ *   gemm_tflops_per_cu  K-loop rate of one CU (256x256 tiles)  5.0
+ *   tile_overhead_us    fixed cost per GEMM tile               20
  *   comm_gbps_per_cu    copy/reduce rate of one workgroup       45
  *   comm_gbps_chip      comm bandwidth of the whole chip        5200
  *   unit_overhead_us    fixed cost per comm unit                1

@@ -88,14 +88,15 @@ def test_chip_ceiling_bounds_the_comm_time():
 ])
 def test_lower_bounds_with_default_rates(op, extra):
     """The makespan is at least the GEMM work over the whole grid at the
-    modelled rate, and the best prediction is one of the candidates."""
+    default modelled rate (5 TFLOP/s per CU), and the best prediction is one
+    of the candidates."""
     grid = 256
     cands = [16, 64, 128, 192, 224, 255]
     best, ms = il.iris_predict_gemm_wgs(op, cands, grid, **extra)
     assert best in cands and ms[best] == min(ms.values())
     M, N = extra["M"], extra["N"]
     K = extra["K"] * (extra["W"] if op == il.IRIS_OP_AG_MM else 1)
-    gemm_ms = 2.0 * M * N * K / (4.4e12 * grid) * 1e3
+    gemm_ms = 2.0 * M * N * K / (5.0e12 * grid) * 1e3
     for v in ms.values():
         assert v >= gemm_ms * (1 - 1e-6)
 
