@@ -66,7 +66,7 @@ struct CommArgs {
 // an L2 write-back (the fused op); the sequential copy kernel uses plain
 // stores.
 template <int U, bool COHERENT>
-__device__ void ag_copy_unit(const CommArgs& a, int pm, int s, int q) {
+__device__ void ag_copy_unit(const CommArgs& a, int pm, int s, int q, uint32_t part = 0, uint32_t nparts = 1) {
   const int r0 = pm * a.BM + q * a.rows_u;
   const int rows = min(a.rows_u, a.M - r0);
   if (rows <= 0) return;
@@ -78,7 +78,7 @@ __device__ void ag_copy_unit(const CommArgs& a, int pm, int s, int q) {
   // the unit's stores span (rows - 1) * K + K_local elements from dst; the
   // host keeps rows_u * K * 2 below 2^31 bytes
   const auto rdst = make_rsrc(dst, (uint32_t)(((int64_t)(rows - 1) * a.K + a.K_local) * 2));
-  for (uint32_t base = threadIdx.x; base < total; base += kThreads * U) {
+  for (uint32_t base = threadIdx.x + part * kThreads * U; base < total; base += kThreads * U * nparts) {
     u32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -145,7 +145,7 @@ __device__ __forceinline__ void accumulate(float (&acc)[U][8], const f16* const*
 // [cc*comm_bn, +comm_bn) of the (M x ncols) output; own values come from C
 // at column offset col0.
 template <int U>
-__device__ void reduce2d_unit(const CommArgs& a, int pm, int q, int cc) {
+__device__ void reduce2d_unit(const CommArgs& a, int pm, int q, int cc, uint32_t part = 0, uint32_t nparts = 1) {
   const int r0 = pm * a.BM + q * a.rows_u;
   const int rows = min(a.rows_u, a.M - r0);
   const int j0 = cc * a.comm_bn;
@@ -154,7 +154,7 @@ __device__ void reduce2d_unit(const CommArgs& a, int pm, int q, int cc) {
   const uint32_t vpr = (uint32_t)(cols >> 3);
   const uint32_t total = (uint32_t)rows * vpr;
   const FastDiv fd = FastDiv::make(vpr);
-  for (uint32_t base = threadIdx.x; base < total; base += kThreads * U) {
+  for (uint32_t base = threadIdx.x + part * kThreads * U; base < total; base += kThreads * U * nparts) {
     float acc[U][8];
     int64_t orow[U];
     bool ok[U];
@@ -185,12 +185,12 @@ __device__ void reduce2d_unit(const CommArgs& a, int pm, int q, int cc) {
 // ----------------------------------------------------------- flat reduce
 // Unit u: elements [u*chunk, min((u+1)*chunk, elems)); dst = sum_w src[w].
 template <int U>
-__device__ void reduce_flat_unit(const CommArgs& a, int u) {
+__device__ void reduce_flat_unit(const CommArgs& a, int u, uint32_t part = 0, uint32_t nparts = 1) {
   const int64_t e0 = (int64_t)u * a.chunk;
   const int64_t n = min((int64_t)a.chunk, a.elems - e0);
   if (n <= 0) return;
   const uint32_t total = (uint32_t)(n >> 3);
-  for (uint32_t base = threadIdx.x; base < total; base += kThreads * U) {
+  for (uint32_t base = threadIdx.x + part * kThreads * U; base < total; base += kThreads * U * nparts) {
     float acc[U][8];
     int64_t idx[U];
     bool ok[U];
@@ -211,14 +211,14 @@ __device__ void reduce_flat_unit(const CommArgs& a, int u) {
 // ------------------------------------------------------------- block copy
 // Unit (w, c): elements [c*chunk, min((c+1)*chunk, blk)) of source w.
 template <int U>
-__device__ void copy_block_unit(const CommArgs& a, int w, int c) {
+__device__ void copy_block_unit(const CommArgs& a, int w, int c, uint32_t part = 0, uint32_t nparts = 1) {
   const int64_t e0 = (int64_t)c * a.chunk;
   const int64_t n = min((int64_t)a.chunk, a.blk - e0);
   if (n <= 0) return;
   const uint32_t total = (uint32_t)(n >> 3);
   const f16* src = a.src[w] + e0;
   f16* dst = a.dst + (int64_t)a.dst_blk[w] * a.blk + e0;
-  for (uint32_t base = threadIdx.x; base < total; base += kThreads * U) {
+  for (uint32_t base = threadIdx.x + part * kThreads * U; base < total; base += kThreads * U * nparts) {
     u32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {

@@ -107,8 +107,10 @@ __device__ __forceinline__ void backoff(int& n) {
 }
 
 // ------------------------------------------------------------ comm units
+// Unit u; with nparts > 1 only the part-th of every nparts vector groups
+// (a workgroup of the sequential comm kernel sharing the unit with others).
 template <int OP, bool FUSED = true>
-__device__ void run_comm_unit(const Params& p, int u) {
+__device__ void run_comm_unit(const Params& p, int u, uint32_t part = 0, uint32_t nparts = 1) {
   const CommArgs& c = p.c;
   if constexpr (OP == OP_AG) {
     // u = (pm * W + s) * n_sub + q
@@ -116,17 +118,17 @@ __device__ void run_comm_unit(const Params& p, int u) {
     const int pm = u / per_block;
     const int r = u - pm * per_block;
     const int s = r / c.n_sub;
-    ag_copy_unit<8, FUSED>(c, pm, s, r - s * c.n_sub);
+    ag_copy_unit<8, FUSED>(c, pm, s, r - s * c.n_sub, part, nparts);
   } else if constexpr (OP == OP_RS || OP == OP_ARMM) {
     // u = (pm * n_sub + q) * n_cc + cc
     const int slice = u / c.n_cc;
     const int pm = slice / c.n_sub;
-    reduce2d_unit<2>(c, pm, slice - pm * c.n_sub, u - slice * c.n_cc);
+    reduce2d_unit<2>(c, pm, slice - pm * c.n_sub, u - slice * c.n_cc, part, nparts);
   } else if constexpr (OP == OP_CONC_AR) {
-    reduce_flat_unit<2>(c, u);
+    reduce_flat_unit<2>(c, u, part, nparts);
   } else if constexpr (OP == OP_CONC_COPY) {
     const int w = u / c.n_chunk;
-    copy_block_unit<8>(c, w, u - w * c.n_chunk);
+    copy_block_unit<8>(c, w, u - w * c.n_chunk, part, nparts);
   }
 }
 
@@ -321,9 +323,13 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(Params p) {
 template <int OP>
 __global__ __launch_bounds__(kThreads) void comm_only_kernel(Params p) {
   uint64_t cs = ~0ull, ce = 0;
-  for (int u = blockIdx.x; u < p.T_comm; u += gridDim.x) {
+  // fewer units than workgroups: each unit is shared by nparts workgroups
+  const uint32_t nparts = (uint32_t)max(1, (int)gridDim.x / max(1, p.T_comm));
+  const int64_t n_virtual = (int64_t)p.T_comm * nparts;
+  for (int64_t v = blockIdx.x; v < n_virtual; v += gridDim.x) {
     if (cs == ~0ull) cs = stamp_now();
-    run_comm_unit<OP, false>(p, u);
+    const int u = (int)(v / nparts);
+    run_comm_unit<OP, false>(p, u, (uint32_t)(v - (int64_t)u * nparts), nparts);
     ce = stamp_now();
   }
   if (threadIdx.x == 0) {
