@@ -308,8 +308,14 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(Params p) {
     st[1] = ge;
     st[2] = cs;
     st[3] = ce;
-    // everything this workgroup did to the counters and flags precedes this
-    const int done = __hip_atomic_fetch_add(p.ws + kDone, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    // Every counter and flag access of this workgroup was made by this
+    // thread, at agent scope; once they have completed (the drain) none can
+    // follow the count below, so the last workgroup's reset cannot race
+    // them. A release here (an L2 write-back per workgroup, of the C tiles
+    // just stored) cost about 3 us per launch and orders nothing needed: the
+    // kernel's end publishes C.
+    drain_vmem();
+    const int done = __hip_atomic_fetch_add(p.ws + kDone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     slot[0] = (done == (int)gridDim.x - 1);
   }
   __syncthreads();
