@@ -91,9 +91,6 @@ struct FastDiv {
 __device__ __forceinline__ int ld_relaxed(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_release(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ void fence_acquire() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
