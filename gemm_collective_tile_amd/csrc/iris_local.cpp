@@ -519,6 +519,11 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
   p.ws = (int32_t*)((char*)ws + kStampBytes);
   p.comm_stamps = p.stamps + (size_t)kMaxGrid * 4;
   p.spin_limit = 1u << 24;
+  if (const char* sl = getenv("IRIS_LOCAL_SPIN_LIMIT")) {
+    char* end = nullptr;
+    const long v = strtol(sl, &end, 10);
+    if (end != sl && v >= 0 && v <= (1L << 30)) p.spin_limit = (uint32_t)v;
+  }
   p.n_reset = (int)(ibytes / 4);
   p.steal = (r.flags & IRIS_FLAG_NO_STEAL) ? 0 : 1;
   const hipStream_t s = (hipStream_t)stream;

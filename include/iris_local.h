@@ -74,6 +74,17 @@ typedef enum iris_status {
   IRIS_ERR_DEVICE_TIMEOUT = 9 /* a bounded device-side wait expired */
 } iris_status;
 
+/*
+ * Every device-side wait (a GEMM tile for its gathered rows, a reduce unit
+ * for its tiles) polls at most a bounded number of times, then records an
+ * error word in the workspace and goes on, so every launch ends. With the
+ * environment variable IRIS_LOCAL_DEBUG set, each op synchronizes its
+ * stream, reads that word, and returns IRIS_ERR_DEVICE_TIMEOUT if it was
+ * set (the outputs of that call are then not to be trusted).
+ * IRIS_LOCAL_SPIN_LIMIT=n (n >= 0) sets the poll bound (default 2^24), so
+ * that the error path can be exercised.
+ */
+
 /* execution modes ([PR544] description) */
 #define IRIS_MODE_FUSED 0      /* one persistent kernel, two work queues */
 #define IRIS_MODE_SEQUENTIAL 1 /* comm kernel and GEMM kernel, one after the

@@ -366,3 +366,25 @@ def test_tune_gemm_wgs_and_top_k(tmp_path, monkeypatch):
         assert_close(C, Cref, f"C after tuning top_k={top_k}")
         C2, G2 = run_ag(inp)  # uses the tuned split from the cache
         assert_bits_equal(C2, C, f"tuned default top_k={top_k}")
+
+
+def test_device_wait_bound_reports_timeout(monkeypatch):
+    """The host forces a zero poll bound: reduce units that must wait for
+    GEMM tiles give up at once, the launch still ends, and the debug check
+    reports IRIS_ERR_DEVICE_TIMEOUT. With the bound back at its default the
+    same call is correct again (the error word was cleared)."""
+    W, M, N, K = 4, 2048, 2048, 4096
+    inp = rs_inputs(M, N, K, W, seed=31)
+    ref = oracle.matmul_reduce_scatter(host(inp["A"]), host(inp["B"]), [host(p) for p in inp["partials"]],
+                                       W, rank=0, bias=host(inp["bias"]))
+    cfg = Config(gemm_wgs=1)  # nearly every workgroup starts on the reduce units and must wait
+    monkeypatch.setenv("IRIS_LOCAL_DEBUG", "1")
+    monkeypatch.setenv("IRIS_LOCAL_SPIN_LIMIT", "0")
+    note("mm_rs with a zero poll bound (expect IRIS_ERR_DEVICE_TIMEOUT)")
+    with pytest.raises(il.IrisError) as ei:
+        run_rs(inp, W, 0, cfg)
+    assert ei.value.status == 9, ei.value
+    monkeypatch.delenv("IRIS_LOCAL_SPIN_LIMIT")
+    note("mm_rs with the default poll bound")
+    out, _ = run_rs(inp, W, 0, cfg)
+    assert_close(out, ref, "reduce_scatter after a timed-out call")
