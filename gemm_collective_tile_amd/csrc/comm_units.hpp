@@ -186,7 +186,8 @@ __device__ void reduce2d_unit(const CommArgs& a, int pm, int q, int cc, uint32_t
 
 // ----------------------------------------------------------- flat reduce
 // Unit u: elements [u*chunk, min((u+1)*chunk, elems)); dst = sum_w src[w].
-template <int U>
+// U vectors per thread, loads of NB sources in flight at a time.
+template <int U, int NB>
 __device__ void reduce_flat_unit(const CommArgs& a, int u, uint32_t part = 0, uint32_t nparts = 1) {
   const int64_t e0 = (int64_t)u * a.chunk;
   const int64_t n = min((int64_t)a.chunk, a.elems - e0);
@@ -203,7 +204,7 @@ __device__ void reduce_flat_unit(const CommArgs& a, int u, uint32_t part = 0, ui
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[v][e] = 0.0f;
     }
-    accumulate<U, 8>(acc, a.src, a.W, idx, ok);
+    accumulate<U, NB>(acc, a.src, a.W, idx, ok);
 #pragma unroll
     for (int v = 0; v < U; ++v)
       if (ok[v]) st16(a.dst + idx[v], round8(acc[v]));
