@@ -111,7 +111,8 @@ class Case:
 
     def sweep_candidates(self):
         # the listed fractions {0.5, 0.75, 0.875} of the grid, plus splits that
-        # start most workgroups on the copy (1/8, 1/4) or on the GEMM (G-1);
+        # start most workgroups on the copy (1/8, 1/4; for all_gather_matmul
+        # also 1) or on the GEMM (G-1);
         # the library adds its static default
         G = self.G_wgs
         fracs = [0.125, 0.25, 0.5, 0.75, 0.875]
@@ -119,6 +120,8 @@ class Case:
             fracs = [0.375, 0.5, 0.625, 0.75, 0.8125, 0.875, 0.9375]
         cands = {max(1, min(G - 1, int(math.floor(f * G)))) for f in fracs}
         cands.add(G - 1)
+        if self.w.op == "ag_mm":
+            cands.add(1)  # every workgroup but one starts on the copy
         return sorted(cands)
 
 

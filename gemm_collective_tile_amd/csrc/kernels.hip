@@ -200,6 +200,36 @@ __device__ void wait_rows(const Params& p, int pm, int* slot, bool& rows_ready) 
   }
 }
 
+// all_gather with more GEMM tiles than workgroups: a workgroup that found
+// the copy queue empty waits until every copy unit has finished before it
+// takes GEMM tiles. Every unit is then held by a running workgroup, so the
+// wait ends. The copy workgroups thus start their tiles within a poll
+// interval of each other, and in every later wave the tiles that share
+// operands run their K loops in step and meet in L2. Joining the GEMM queue
+// one by one as each finished its last unit (up to a unit's time apart), the
+// g2 all_gather_matmul (M=131072, N=K=16384) fetched 155-207 GiB from beyond
+// L2 on MI355X, against 128 GiB for the same tiles started together; with
+// the wait, 141. With a single wave of tiles there is no later wave to keep
+// in step, and the polling of the finished-unit counter by the waiting
+// workgroups slowed the last copy units (pow2_4k 4096^3: +5 us).
+template <int OP>
+__device__ void wait_all_units(const Params& p, bool& rows_ready) {
+  if (threadIdx.x == 0) {
+    uint32_t polls = 0;
+    int pause = 1;
+    while (ld_relaxed(p.ws + kCommDone) < p.T_comm) {
+      if (++polls > p.spin_limit) {
+        __hip_atomic_store(p.ws + kErr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      backoff(pause);
+    }
+    fence_acquire();
+  }
+  __syncthreads();
+  rows_ready = true;
+}
+
 // A reduce unit waits for the GEMM tiles covering its rows and columns.
 template <int OP, class S>
 __device__ void wait_tiles(const Params& p, int u, int* slot, char* lds) {
@@ -285,6 +315,9 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(Params p) {
     if (phase == 1 && !p.steal) break;
     const bool do_gemm = (phase == 0) == gemm_first;
     if (do_gemm) {
+      if constexpr (OP == OP_AG) {
+        if (p.fused && phase == 1 && p.T_gemm > (int)gridDim.x) wait_all_units<OP>(p, rows_ready);
+      }
       while (true) {
         const int t = claim_gemm(p, home, gone, slot);
         if (t < 0) break;

@@ -8,10 +8,12 @@
 //
 // The simulation replays the kernel's own rules: workgroups below gemm_wgs
 // start on the GEMM queue, the others on the comm queue, and each switches
-// queues when its first one runs dry; a GEMM tile of all_gather_matmul waits
-// for the copy units of its row block and takes unclaimed copy units while
-// it waits; a reduce unit waits for the GEMM tiles of its columns, taking
-// GEMM tiles only while one it needs is still unclaimed. Durations come from
+// queues when its first one runs dry (with more tiles than workgroups, an
+// all_gather_matmul copy workgroup only once every copy unit has finished);
+// a GEMM tile of all_gather_matmul waits for the copy units of its row block
+// and takes unclaimed copy units while it waits; a reduce unit waits for the
+// GEMM tiles of its columns, taking GEMM tiles only while one it needs is
+// still unclaimed. Durations come from
 // a linear model (per-CU GEMM rate, per-workgroup copy/reduce rate, a
 // whole-chip ceiling on the comm bandwidth shared by the units in flight,
 // fixed costs per tile and per unit); the defaults were measured on MI355X.
@@ -157,6 +159,17 @@ double simulate(const Work& w, int gemm_wgs) {
       }
       if (k.phase == 0 && w.steal) {
         k.phase = 1;
+        if (w.kind == 1 && !k.gemm_first && T > w.grid) {
+          // all_gather with more tiles than workgroups: a copy workgroup
+          // joins the GEMM once every copy unit has finished (all are
+          // claimed by now)
+          double all_end = now;
+          for (double e : rb_end) all_end = std::max(all_end, e);
+          if (all_end > now) {
+            ev.push({all_end, i});
+            break;
+          }
+        }
         continue;
       }
       k.done = true;
