@@ -81,6 +81,32 @@ def test_tiny_workload_all_configs():
                 assert_bits_equal(C, first64, f"schedule invariance {cfg}")
 
 
+def test_ag_mm_several_waves_any_split():
+    """More GEMM tiles than workgroups (17 x 17 tiles of 256 x 256 on a grid
+    of 256; 33 x 33 of 128 x 128 on 512), ragged in M and N: copy workgroups
+    join the GEMM only once every copy unit has finished. The gathered matrix
+    is bit-exact, C matches the oracle, and C is bit-identical across splits
+    that start one, some or all but one workgroup on the GEMM, and against
+    sequential mode."""
+    inp = ag_inputs(4196, 4160, 256, 4, seed=21)
+    g_ref, c_ref = oracle_ag(inp)
+    for tile in [(256, 256), (128, 128)]:
+        G = il.iris_grid_size(Config(block_m=tile[0], block_n=tile[1]))
+        n_tiles = -(-4196 // tile[0]) * -(-4160 // tile[1])
+        assert n_tiles > G, (n_tiles, G)
+        first = None
+        for gw, mode in [(1, il.IRIS_MODE_FUSED), (G // 8, il.IRIS_MODE_FUSED), (G // 2, il.IRIS_MODE_FUSED),
+                         (G - 1, il.IRIS_MODE_FUSED), (0, il.IRIS_MODE_SEQUENTIAL)]:
+            note(f"ag_mm several waves tile={tile} grid={G} tiles={n_tiles} gemm_wgs={gw} mode={mode}")
+            C, Gb = run_ag(inp, Config(block_m=tile[0], block_n=tile[1], gemm_wgs=gw, mode=mode))
+            assert_bits_equal(Gb, g_ref, f"gathered tile={tile} gemm_wgs={gw}")
+            if first is None:
+                assert_close(C, c_ref, f"C tile={tile}")
+                first = C
+            else:
+                assert_bits_equal(C, first, f"C invariant tile={tile} gemm_wgs={gw} mode={mode}")
+
+
 @pytest.mark.parametrize("M,N,kl,W", [(256, 256, 256, 2), (300, 200, 40, 3), (64, 72, 8, 1)])
 @pytest.mark.parametrize("tile", TILES)
 def test_ag_mm_integer_exact(M, N, kl, W, tile):
