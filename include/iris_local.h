@@ -129,7 +129,12 @@ typedef enum iris_status {
  *   group_m           rows of tiles per swizzle group. Default 8.
  *   gemm_wgs          workgroups that start on the GEMM queue in fused mode,
  *                     1..G-1 where G = iris_grid_size(op, cfg). Default
- *                     7/8 of G.
+ *                     7/8 of G. The others start on the comm queue and
+ *                     take GEMM tiles once it is empty (unless
+ *                     IRIS_FLAG_NO_STEAL); in iris_ag_mm with more GEMM
+ *                     tiles than G they take tiles only after every copy
+ *                     unit has finished, so that they start in step. Any
+ *                     value gives bit-identical results.
  *   comm_block_m      rows per comm unit (all_gather copy and the
  *                     reduce of reduce_scatter / matmul_all_reduce); must
  *                     divide block_m. Default: the largest power of two
