@@ -45,25 +45,58 @@ __device__ __forceinline__ int xcd_id() {
   return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (15 << 11)) & (kXcds - 1);
 }
 
-// GEMM claim: this XCD's queue first, then the others in turn. `gone`
-// (meaningful in thread 0) marks queues this workgroup has seen empty, so
-// each queue's counter overshoots its share by at most one per workgroup.
+// GEMM claim: this XCD's queue first (thread 0, one atomic), then the
+// others. `gone` (bit x: queue x seen empty) is kept in thread 0 and handed
+// to wave 0 for the steal, so each queue's counter overshoots its share by at
+// most one per workgroup. Once the home queue is empty, lane x of wave 0
+// reads queue x's counter (one round trip for all eight) and only a queue
+// that still shows unclaimed tiles gets an atomic: trying the other queues
+// one atomic at a time put up to eight serial round trips at the end of
+// every workgroup's GEMM phase.
 __device__ __forceinline__ int claim_gemm(const Params& p, int home, uint32_t& gone, int* slot) {
   if (threadIdx.x == 0) {
     int t = -1;
-    for (int i = 0; i < kXcds && t < 0; ++i) {
-      const int x = (home + i) & (kXcds - 1);
-      if (gone & (1u << x)) continue;
-      const int c = xcd_tile(p.xcd_q, x, fetch_add(p.ws + kCtrGemm + x * kLine, 1));
+    if (!(gone & (1u << home))) {
+      const int c = xcd_tile(p.xcd_q, home, fetch_add(p.ws + kCtrGemm + home * kLine, 1));
       if (c < p.T_gemm)
         t = c;
       else
-        gone |= 1u << x;
+        gone |= 1u << home;
     }
     slot[0] = t;
+    slot[1] = (int)gone;
   }
   __syncthreads();
-  const int v = slot[0];
+  int v = slot[0];
+  if (v < 0 && threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    uint32_t g = (uint32_t)slot[1];
+    while (g != (1u << kXcds) - 1) {
+      bool open = false;
+      if (lane < kXcds && !(g & (1u << lane)))
+        open = xcd_tile(p.xcd_q, lane, ld_relaxed(p.ws + kCtrGemm + lane * kLine)) < p.T_gemm;
+      const uint32_t m = (uint32_t)__ballot(open) & ((1u << kXcds) - 1);
+      g |= ~m & ((1u << kXcds) - 1);  // counters only grow: these stay empty
+      if (m == 0) break;
+      const int s = (home + 1) & (kXcds - 1);  // first open queue after home
+      const uint32_t rot = ((m >> s) | (m << (kXcds - s))) & ((1u << kXcds) - 1);
+      const int pick = (s + __builtin_ctz(rot)) & (kXcds - 1);
+      int c = 0;
+      if (lane == 0) c = xcd_tile(p.xcd_q, pick, fetch_add(p.ws + kCtrGemm + pick * kLine, 1));
+      c = __shfl(c, 0);
+      if (c < p.T_gemm) {
+        v = c;
+        break;
+      }
+      g |= 1u << pick;
+    }
+    if (lane == 0) {
+      gone = g;
+      slot[0] = v;
+    }
+  }
+  __syncthreads();
+  v = slot[0];
   __syncthreads();
   return v;
 }
