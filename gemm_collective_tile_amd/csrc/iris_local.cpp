@@ -402,6 +402,11 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
     return fail(IRIS_ERR_CONFIG,
                 "two-stream mode needs an op whose GEMM and collective are independent "
                 "(iris_concurrent, iris_mm_ag_local)");
+  // the tile count depends on the shape and the tile only: checked before
+  // any device call, like every other argument
+  if (((d.M + r.bm - 1) / r.bm) * ((d.N + r.bn - 1) / r.bn) > (1 << 30))
+    return fail(IRIS_ERR_UNSUPPORTED, "too many GEMM tiles (%lld; limit 2^30)",
+                (long long)(((d.M + r.bm - 1) / r.bm) * ((d.N + r.bn - 1) / r.bn)));
   int dev = 0;
   DevInfo di;
   st = current_device(&dev, &di);
@@ -451,8 +456,6 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
   p.order.n_pm = n_pm;
   p.order.n_pn = n_pn;
   p.order.group_m = r.gm;
-  if ((int64_t)n_pm * n_pn > (1 << 30))
-    return fail(IRIS_ERR_UNSUPPORTED, "too many GEMM tiles (%lld; limit 2^30)", (long long)n_pm * n_pn);
   p.T_gemm = n_pm * n_pn;
   p.xcd_q = std::max(1, r.grid / iris::kXcds);
   iris::CommArgs& c = p.c;

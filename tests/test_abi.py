@@ -83,8 +83,16 @@ def test_ag_mm_argument_errors(lib):
     assert b"K_local" in lib.iris_last_error_message()
     assert call(N=100) == 4         # N % 8
     assert call(M=0) == 1
+    assert call(M=-256) == 1
     assert call(bias=MIS) == 4
     assert b"bias" in lib.iris_last_error_message()
+    # size limits (buffer resources and tile indices are 32-bit): rejected
+    # before any device call
+    assert call(M=(1 << 30) + 256) == 2
+    assert call(N=(1 << 21) + 8) == 2
+    assert call(K=(1 << 20) + 8) == 2   # W * K_local = K past 2^21
+    assert b"too large" in lib.iris_last_error_message()
+    assert call(M=1 << 30, N=1 << 21) == 2  # 2^22 * 2^13 tiles past 2^30
 
 
 def test_rs_ar_concurrent_argument_errors(lib):
