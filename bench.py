@@ -267,11 +267,35 @@ def cpu_baseline(case):
     }, bad, gathered_ok
 
 
+def strip_comments(src):
+    """C++ source without // and /* */ comments and with runs of blank space
+    collapsed, so that a comment edit leaves the hash of the code alone."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif src[i] in "\"'":  # string or character literal, copied whole
+            q, j = src[i], i + 1
+            while j < n and src[j] != q:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(src[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash():
+    """Hash of the kernel sources' code (comments and layout ignored)."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "gemm_collective_tile_amd", "csrc", f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+        with open(os.path.join(ROOT, "gemm_collective_tile_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(f.encode() + b"\0" + strip_comments(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

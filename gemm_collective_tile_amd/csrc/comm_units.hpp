@@ -28,9 +28,11 @@
 // once by a reduce (partials, buffers) uses the streaming cache policy; its
 // results are stored with the default policy (streaming stores ran the
 // all_reduce of 8 x 64Mi fp16 at 5.1 TB/s on MI355X, default ones at 5.5).
-// The copy keeps the default policy both ways: its shards are small enough
-// to stay in the last-level cache between calls, and the GEMM reads the
-// gathered matrix next.
+// The all_gather copy loads with the default policy (pow2_4k's shards stay
+// in the last-level cache between calls; streaming loads made that copy
+// slower). It stores with the agent-coherent policy in the fused op, so that
+// a unit can be published without an L2 write-back, and with the default
+// policy in the sequential copy kernel.
 #pragma once
 
 #include "device_common.hpp"
