@@ -30,8 +30,10 @@
 namespace iris {
 
 // ------------------------------------------------------------------ queues
-// One atomic per claim. A workgroup leaves a queue the first time it comes
-// back empty, so a counter overshoots its total by at most the grid size.
+// One atomic per claim. A workgroup leaves a queue the first time a claim
+// comes back empty; a waiting workgroup helps with an atomic only after a
+// read shows unclaimed work. A counter thus overshoots its total by a few
+// claims per workgroup at most, far from int32 overflow (totals <= 2^30).
 __device__ __forceinline__ int claim(int* ctr, int T, int* slot) {
   if (threadIdx.x == 0) slot[0] = fetch_add(ctr, 1);
   __syncthreads();
