@@ -2,9 +2,11 @@
 
 Each expected makespan below is worked out by hand from the scheduling rules
 the predictor replays (workgroups below gemm_wgs start on the GEMM queue, the
-rest on the comm queue, each switches queues once; an all_gather_matmul tile
-waits for the copy units of its row block and takes copy units meanwhile; a
-reduce unit waits for the tiles of its columns), with a rate model chosen so
+rest on the comm queue, each switches queues once, an all_gather_matmul copy
+workgroup with more tiles than workgroups only after the whole gather; an
+all_gather_matmul tile waits for the copy units of its row block and takes
+copy units meanwhile; a reduce unit waits for the tiles of its columns),
+with a rate model chosen so
 the durations are round numbers:
 
     GEMM tile  = 2*rows*cols*K / (1 TFLOP/s)          (no fixed cost)
@@ -58,6 +60,24 @@ def test_all_gather_tile_waits_for_its_row_block():
     # The GEMM workgroup holds the tile and copies one unit while the other copies the second.
     _, ms = predict(il.IRIS_OP_AG_MM, [1], 2, Config(comm_block_m=256), W=2, M=256, N=256, K=256)
     assert ms[1] == pytest.approx(unit_ms(256 * 256 * 4) + tile_ms(256, 256, 512), rel=1e-6)
+
+
+def test_all_gather_copy_workgroups_join_after_the_whole_gather():
+    # More tiles than workgroups: a workgroup that started on the copy takes
+    # GEMM tiles only once every copy unit has finished. Grid 3, gemm_wgs 1,
+    # W=2, M=512 (row blocks 0 and 1), N=2048 (8 column tiles), GROUP_M 1 (row
+    # block 0's tiles t0..t7 first), one 256-row copy unit per (row block,
+    # shard): u0, u1 (block 0), u2, u3 (block 1), each U; a tile takes t =
+    # 0.256 U. t=0: wg0 holds t0 and copies u0, wg1 copies u1, wg2 u2. t=U:
+    # wg0 runs t0, wg1 copies u3 (until 2U), wg2 finds the copy queue empty
+    # and waits for u3. wg0 runs t0..t3 alone (until U+4t = 2.024 U); from 2U
+    # all three take tiles: wg1, wg2: t4, t5 | t7, t8 | t10, t11 | t13, t14;
+    # wg0: t6, t9, t12, t15, the last ending at U + 8t. (Joining at U would
+    # have given U + 7t.)
+    U, t = unit_ms(256 * 256 * 4), tile_ms(256, 256, 512)
+    assert t == pytest.approx(0.256 * U)
+    _, ms = predict(il.IRIS_OP_AG_MM, [1], 3, Config(comm_block_m=256, group_m=1), W=2, M=512, N=2048, K=256)
+    assert ms[1] == pytest.approx(U + 8 * t, rel=1e-6)
 
 
 def test_reduce_scatter_units_wait_for_their_tiles():
