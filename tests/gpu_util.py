@@ -48,6 +48,14 @@ def assert_bits_equal(a: torch.Tensor, b, what: str) -> None:
         raise AssertionError(f"{what}: {len(diff)} elements differ bitwise, first at {tuple(diff[0])}")
 
 
+def assert_same_bits(a: torch.Tensor, b: torch.Tensor, what: str) -> None:
+    """Two device tensors hold the same bits (compared on the device)."""
+    ai, bi = a.view(torch.int16), b.view(torch.int16)
+    if not torch.equal(ai, bi):
+        n = int((ai != bi).sum().item())
+        raise AssertionError(f"{what}: {n} elements differ bitwise")
+
+
 def assert_exact(got: torch.Tensor, ref: np.ndarray, what: str) -> None:
     """Integer-exact case: the fp16 result must equal the exact value."""
     assert np.all(np.abs(ref) <= 2048), f"{what}: exact values exceed the fp16 integer range"

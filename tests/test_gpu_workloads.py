@@ -1,5 +1,6 @@
 """Parity at the full workload sizes, in the launch configurations bench.py
-times (default 256x256 tiles; the gemm_wgs candidates of its sweep).
+times (default 256x256 tiles; the gemm_wgs candidates of its sweep, or at
+least the split it picks, compared bit for bit with the default split).
 
 Large GEMM outputs are checked on 64 sampled 128x128 tiles (always including
 the first and the last) computed one by one by the oracle; the copy and
@@ -14,7 +15,7 @@ import torch
 
 import oracle
 import workloads as wl
-from gpu_util import assert_bits_equal, assert_close, host, note
+from gpu_util import assert_bits_equal, assert_close, assert_same_bits, host, note
 
 pytestmark = pytest.mark.gpu
 
@@ -29,9 +30,16 @@ TILE = 128
 NTILES = 64
 
 
-def sweep_candidates():
+def sweep_candidates(ag=True):
+    """The splits bench.py's sweep tries: the fractions {0.5, 0.75, 0.875} of
+    the grid the pow2_4k configuration lists, 1/8, 1/4, G-1 and, for
+    all_gather_matmul, 1."""
     G = il.iris_grid_size(None)
-    return sorted({max(1, min(G - 1, int(math.floor(f * G)))) for f in (0.5, 0.75, 0.875)})
+    c = {max(1, min(G - 1, int(math.floor(f * G)))) for f in (0.125, 0.25, 0.5, 0.75, 0.875)}
+    c.add(G - 1)
+    if ag:
+        c.add(1)
+    return sorted(c)
 
 
 def check_sampled_tiles(C: torch.Tensor, ref_fn, what: str) -> None:
@@ -78,7 +86,7 @@ def test_pow2_4k_all_gather_matmul():
             check_sampled_tiles(C, ref, "pow2_4k C")
             first = C
         else:
-            assert_bits_equal(C, first, f"schedule invariance gemm_wgs={gw}")
+            assert_same_bits(C, first, f"schedule invariance gemm_wgs={gw}")
 
 
 def test_llama7b_gate_reduce_scatter():
@@ -89,6 +97,17 @@ def test_llama7b_gate_reduce_scatter():
     out = torch.full((w.M, w.N_local), float("nan"), dtype=torch.float16, device="cuda")
     il.iris_mm_rs_local(out, C, inp["A"], inp["B"], inp["partials"], w.W, rank=w.rank, bias=inp["bias"])
     torch.cuda.synchronize()
+    # the split the bench picks for this shape (every workgroup but one
+    # starts on the GEMM): bit-identical to the default split
+    G = il.iris_grid_size(None, op=il.IRIS_OP_MM_RS)
+    note(f"llama7b_gate fused reduce_scatter gemm_wgs={G - 1}")
+    C2, out2 = torch.full_like(C, float("nan")), torch.full_like(out, float("nan"))
+    il.iris_mm_rs_local(out2, C2, inp["A"], inp["B"], inp["partials"], w.W, rank=w.rank, bias=inp["bias"],
+                        config=Config(gemm_wgs=G - 1))
+    torch.cuda.synchronize()
+    assert_same_bits(out2, out, f"reduce_scatter out, gemm_wgs={G - 1} against the default split")
+    assert_same_bits(C2, C, f"C, gemm_wgs={G - 1} against the default split")
+    del C2, out2
     A, B, bias = host(inp["A"]), host(inp["B"]), host(inp["bias"])
     note("llama7b_gate oracle: full reduce_scatter slice")
     ref = oracle.matmul_reduce_scatter(A, B, [host(p) for p in inp["partials"]], w.W, rank=w.rank,
@@ -106,6 +125,17 @@ def test_concurrent_gemm_and_all_reduce():
     out = torch.full((w.comm_elems,), float("nan"), dtype=torch.float16, device="cuda")
     il.iris_concurrent(C, inp["A"], inp["B"], out, inp["comm_in"], bias=inp["bias"])
     torch.cuda.synchronize()
+    # other splits of the bench's sweep for this op: bit-identical results
+    G = il.iris_grid_size(None, op=il.IRIS_OP_CONCURRENT)
+    for gw in ((G * 13) // 16, (G * 15) // 16):
+        note(f"concurrent fused gemm_wgs={gw}")
+        C2, out2 = torch.full_like(C, float("nan")), torch.full_like(out, float("nan"))
+        il.iris_concurrent(C2, inp["A"], inp["B"], out2, inp["comm_in"], bias=inp["bias"],
+                           config=Config(gemm_wgs=gw))
+        torch.cuda.synchronize()
+        assert_same_bits(C2, C, f"concurrent C, gemm_wgs={gw} against the default split")
+        assert_same_bits(out2, out, f"all_reduce, gemm_wgs={gw} against the default split")
+        del C2, out2
     note("concurrent oracle: full all_reduce")
     aref = oracle.all_reduce([host(x) for x in inp["comm_in"]])
     assert_close(out, aref, "all_reduce (full)")
@@ -123,6 +153,16 @@ def test_g2_all_gather_matmul():
     G = torch.full((w.M, w.K), float("nan"), dtype=torch.float16, device="cuda")
     il.iris_ag_mm(C, G, inp["shards"], inp["B"], inp["bias"])
     torch.cuda.synchronize()
+    # the split the bench picks for this shape (every workgroup but one
+    # starts on the copy, and joins the GEMM after the whole gather):
+    # bit-identical to the default split
+    note("g2 fused all_gather_matmul gemm_wgs=1")
+    C2, G2 = torch.full_like(C, float("nan")), torch.full_like(G, float("nan"))
+    il.iris_ag_mm(C2, G2, inp["shards"], inp["B"], inp["bias"], config=Config(gemm_wgs=1))
+    torch.cuda.synchronize()
+    assert_same_bits(C2, C, "g2 C, gemm_wgs=1 against the default split")
+    assert_same_bits(G2, G, "g2 gathered, gemm_wgs=1 against the default split")
+    del C2, G2
     note("g2: full gathered buffer")
     check_gathered(G, inp["shards"])
     note("g2: 64 sampled tiles of C")
