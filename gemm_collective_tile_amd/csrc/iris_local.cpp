@@ -538,6 +538,13 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
     p.op = d.kind;
     p.fused = 1;
     p.gemm_wgs = r.gemm_wgs;
+    // beside an independent collective only the gemm_wgs workgroups that
+    // start on the GEMM run tiles for most of the launch: deal the XCD queues
+    // in blocks of their number per XCD, so that the tiles an XCD runs at once
+    // form whole patches (the concurrent 8192^3 GEMM at gemm_wgs 224:
+    // 0.5-1.5 % faster on MI355X); the dependent ops run the GEMM on every
+    // workgroup and keep blocks of grid / 8
+    if (d.kind == iris::OP_CONC_AR || d.kind == iris::OP_CONC_COPY) p.xcd_q = std::max(1, r.gemm_wgs / iris::kXcds);
     e = iris::launch_persistent(p, r.bm, r.bn, r.grid, s);
     if (e != hipSuccess) return hip_fail(e, "fused launch");
   } else if (r.mode == IRIS_MODE_TWO_STREAM) {
