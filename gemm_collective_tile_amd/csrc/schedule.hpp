@@ -60,7 +60,8 @@ __host__ __device__ inline int tile_index(const TileOrder& o, int pm, int pn) {
 // MI355X has 8 XCDs, each with its own L2, and hands workgroups to them
 // round-robin. The tile sequence above is dealt to one queue per XCD in
 // blocks of Q consecutive tiles: block b goes to XCD b mod 8. With Q about
-// the number of workgroups an XCD holds, the tiles an XCD runs at once form
+// the number of workgroups an XCD runs GEMM tiles on (grid / 8, or
+// gemm_wgs / 8 beside an independent collective), the tiles an XCD runs at once form
 // one compact patch of the grouped order (at Q = 32 and GROUP_M = 8, 8 row
 // blocks x 4 column tiles), so their A rows and B columns meet in that XCD's
 // L2 instead of being fetched by all eight.
