@@ -130,7 +130,7 @@ __device__ __forceinline__ void publish_count_coherent(int* a, int* b) {
   release_begin();
   if (threadIdx.x == 0) {
     fetch_add(a, 1);
-    fetch_add(b, 1);
+    if (b) fetch_add(b, 1);
   }
 }
 
@@ -183,7 +183,14 @@ __device__ __forceinline__ int ag_unit_block(const Params& p, int u) { return u 
 template <int OP>
 __device__ __forceinline__ void finish_comm_unit(const Params& p, int u) {
   if constexpr (OP == OP_AG) {
-    if (p.fused) publish_count_coherent(p.ws + kFlagBase + ag_unit_block(p, u) * kLine, p.ws + kCommDone);
+    // the finished-unit count only serves a GEMM with more tiles than
+    // workgroups (tiles that no longer check their row block; the copy
+    // workgroups' wait before joining the GEMM): with a single wave every
+    // workgroup has about one tile, and traffic on that one line while the
+    // last units land slowed them (pow2_4k)
+    if (p.fused)
+      publish_count_coherent(p.ws + kFlagBase + ag_unit_block(p, u) * kLine,
+                             p.T_gemm > (int)gridDim.x ? p.ws + kCommDone : nullptr);
   }
 }
 
@@ -204,7 +211,7 @@ __device__ void wait_rows(const Params& p, int pm, int* slot, bool& rows_ready) 
   while (true) {
     if (threadIdx.x == 0) {
       int ready = 0, help = -1;
-      const int all = ld_relaxed(p.ws + kCommDone);
+      const int all = p.T_gemm > (int)gridDim.x ? ld_relaxed(p.ws + kCommDone) : 0;
       const int have = ld_relaxed(cnt);
       if (all >= p.T_comm) {
         ready = 2;
