@@ -15,8 +15,10 @@
 // words in the workspace:
 //   all_gather:  rows[pm] counts the finished copy units of GEMM row block
 //                pm; a GEMM tile of that block waits until all W * n_sub
-//                are in. A second counter of all finished units lets a
-//                workgroup that has seen every unit done stop checking.
+//                are in. With more GEMM tiles than workgroups, a second
+//                counter of all finished units lets a workgroup that has
+//                seen every unit done stop checking, and holds the copy
+//                workgroups back until the gather is complete.
 //   reduce:      flag[pm*n_pn + pn] = 1 once GEMM tile (pm, pn) is stored;
 //                a reduce unit waits for the tiles covering its columns.
 // A workgroup that has to wait first takes unclaimed work from the queue it
