@@ -87,7 +87,7 @@ def test_ag_mm_several_waves_any_split():
     join the GEMM only once every copy unit has finished. The gathered matrix
     is bit-exact, C matches the oracle, and C is bit-identical across splits
     that start one, some or all but one workgroup on the GEMM, and against
-    sequential mode."""
+    sequential mode, with copy units of the default size and of one row."""
     inp = ag_inputs(4196, 4160, 256, 4, seed=21)
     g_ref, c_ref = oracle_ag(inp)
     for tile in [(256, 256), (128, 128)]:
@@ -95,10 +95,16 @@ def test_ag_mm_several_waves_any_split():
         n_tiles = -(-4196 // tile[0]) * -(-4160 // tile[1])
         assert n_tiles > G, (n_tiles, G)
         first = None
-        for gw, mode in [(1, il.IRIS_MODE_FUSED), (G // 8, il.IRIS_MODE_FUSED), (G // 2, il.IRIS_MODE_FUSED),
-                         (G - 1, il.IRIS_MODE_FUSED), (0, il.IRIS_MODE_SEQUENTIAL)]:
-            note(f"ag_mm several waves tile={tile} grid={G} tiles={n_tiles} gemm_wgs={gw} mode={mode}")
-            C, Gb = run_ag(inp, Config(block_m=tile[0], block_n=tile[1], gemm_wgs=gw, mode=mode))
+        # comm_block_m = 1: 4196 * 4 one-row copy units, dozens per workgroup,
+        # so the comm loop claims units ahead
+        for gw, mode, rows in [(1, il.IRIS_MODE_FUSED, 0), (G // 8, il.IRIS_MODE_FUSED, 0),
+                               (G // 2, il.IRIS_MODE_FUSED, 0), (G - 1, il.IRIS_MODE_FUSED, 0),
+                               (1, il.IRIS_MODE_FUSED, 1), (G // 2, il.IRIS_MODE_FUSED, 1),
+                               (0, il.IRIS_MODE_SEQUENTIAL, 0)]:
+            note(f"ag_mm several waves tile={tile} grid={G} tiles={n_tiles} gemm_wgs={gw} mode={mode} "
+                 f"comm_block_m={rows}")
+            C, Gb = run_ag(inp, Config(block_m=tile[0], block_n=tile[1], gemm_wgs=gw, mode=mode,
+                                       comm_block_m=rows))
             assert_bits_equal(Gb, g_ref, f"gathered tile={tile} gemm_wgs={gw}")
             if first is None:
                 assert_close(C, c_ref, f"C tile={tile}")
