@@ -127,7 +127,8 @@ __device__ __forceinline__ void publish(int* flag) {
 
 // For data written with agent-coherent stores (buf_store16_coherent): once
 // every wave's stores have completed they are visible on every XCD, so the
-// counters can be bumped with no L2 write-back in between.
+// counters (a, and b unless it is null) can be bumped with no L2 write-back
+// in between.
 __device__ __forceinline__ void publish_count_coherent(int* a, int* b) {
   release_begin();
   if (threadIdx.x == 0) {
