@@ -1,26 +1,35 @@
 """Benchmark of one GPU's share of the fused communication + GEMM ops on MI355X.
 
-One step = one call of the fused op on the headline workload (default
-pow2_4k all_gather_matmul: W=8 K-shards (4096, 512) gathered into (4096,
-4096) and multiplied by B (4096, 4096) plus bias), with every input already
+One step = one call of the fused op on the headline workload (default g2
+all_gather_matmul: W=8 K-shards (131072, 2048) gathered into (131072, 16384)
+and multiplied by B (16384, 16384) plus bias), with every input already
 resident in HBM. The gemm_wgs split is swept first (untimed), as the host
 sweep does for any shape, then `--warmup` untimed and `--steps` timed steps
 run. Prints ONE JSON line.
 
   value      GEMM TFLOP/s of the whole fused op: 2*M*N*K / (wall time per step)
   roofline   the fused persistent kernel against the dense fp16 MFMA peak:
-             2*M*N*K / (average kernel duration from HIP events around each
-             launch on the op's stream). `traffic` is the kernel's HBM bytes
-             per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, scaled by
-             what the same counters read for a plain device copy; it is read
-             from profiles/ and reported only while the kernel sources still
-             hash to the value recorded there (else null)
-  comm       the communication units' HBM GB/s over their in-kernel window
-  cpu_baseline  the CPU oracle on the full headline problem (gather + GEMM +
-             bias in fp64) on the host's cores; also checks the GPU output
-  extra      the other workloads (llama7b_gate reduce_scatter, concurrent
-             8192^3 GEMM beside an all_reduce, g2 all_gather_matmul) measured
-             the same way, unless --headline-only
+             2*M*N*K / (mean kernel duration from HIP events on the op's
+             stream around the timed launches). `traffic` is the kernel's
+             bytes fetched from beyond L2 plus bytes written, per launch, from
+             rocprofv3 FETCH_SIZE / WRITE_SIZE runs scaled by what the same
+             counters read for a plain device copy; read from profiles/ and
+             reported only while the kernel sources still hash to the value
+             recorded there (else null)
+  comm       the communication units' GB/s over their in-kernel window, and
+             the sequential comm kernel's; fractions of the 8 TB/s HBM peak
+             only for data sets larger than the 256 MiB last-level cache
+  clock      the shader clock the GPU held during the fused launch
+             (iris_last_clock), next to the 2.4 GHz of the published peak
+  copy_ceiling  a plain 1 GiB device-to-device copy (torch), GB/s
+  cpu_baseline  the CPU oracle on a bounded sample of the headline workload
+             (sampled 128x128 output tiles computed in fp64, and the whole
+             gathered buffer compared bit for bit) on the CPU share of one GPU
+  oracle_check  every measured workload is checked against the oracle
+             outside the timed regions; any mismatch makes the exit status 1
+  extra      the other workloads (pow2_4k all_gather_matmul, llama7b_gate
+             reduce_scatter, concurrent 8192^3 GEMM beside an all_reduce)
+             measured the same way, unless --headline-only
 
 Only one GPU is used: --gpus above 1 exits with a message.
 """
@@ -38,9 +47,12 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+MALL_BYTES = 256 << 20      # MI355X last-level (Infinity) cache
 KERNEL_SOURCES = ("kernels.hip", "gemm_tile.hpp", "comm_units.hpp", "device_common.hpp", "schedule.hpp",
                   "launch.hpp")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "persistent_kernel_ag_pow2_4k_traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
+EXTRA_WORKLOADS = ("pow2_4k", "llama7b_gate", "concurrent")
+CPU_TILES = 256             # sampled 128x128 output tiles in the CPU baseline
 
 
 def parse():
@@ -48,9 +60,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="pow2_4k")
+    ap.add_argument("--workload", default="g2")
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true", help="skip the oracle checks (profiling runs)")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--gemm-wgs", type=int, default=0,
                     help="fixed gemm_wgs for the headline workload (no sweep)")
@@ -172,6 +185,7 @@ def measure(name, steps, warmup, sweep, fixed_wgs=0):
     wall_ms, mean_ms = time_steps(case, cfg, steps, warmup)
     case.step(cfg)
     gwin, cwin = windows(case)
+    clock_mhz = il.iris_last_clock()
     log(f"[{name}] timing sequential mode")
     seq_cfg = Config(mode=il.IRIS_MODE_SEQUENTIAL)
     case.step(seq_cfg)
@@ -208,7 +222,11 @@ def measure(name, steps, warmup, sweep, fixed_wgs=0):
             log(f"[{name}] timing two-stream mode, gemm_wgs={gw}")
             two[gw] = round(time_steps(case, Config(mode=il.IRIS_MODE_TWO_STREAM, gemm_wgs=gw),
                                        max(3, steps // 2), 2)[0], 4)
+    il.iris_check_device_error()
     flops = w.gemm_flops
+    # comm data that fits in the last-level cache stays there between steps:
+    # its rates are not HBM rates
+    hbm_sized = w.comm_bytes > 2 * MALL_BYTES
     res = {
         "workload": name, "op": w.op, "M": w.M, "N": w.N, "K": w.K, "W": w.W,
         "gemm_wgs": best, "grid": case.G_wgs, "tile": "256x256x64",
@@ -218,12 +236,15 @@ def measure(name, steps, warmup, sweep, fixed_wgs=0):
         "fused_ms": round(wall_ms, 4), "kernel_ms": round(mean_ms, 4),
         "tflops": round(flops / (wall_ms * 1e-3) / 1e12, 2),
         "kernel_tflops": round(flops / (mean_ms * 1e-3) / 1e12, 2),
+        "clock_mhz": round(clock_mhz, 1) if clock_mhz > 0 else None,
         "gemm_window_ms": round(gwin, 4) if gwin else None,
         "comm_window_ms": round(cwin, 4) if cwin else None,
         "comm_bytes": w.comm_bytes,
+        "comm_hbm_sized": hbm_sized,
         "comm_gbps": round(w.comm_bytes / (cwin * 1e-3) / 1e9, 1) if cwin else None,
         "sequential_ms": round(seq_cmp, 4),
         "fused_vs_sequential_ms": [round(fused_cmp, 4), round(seq_cmp, 4)],
+        "fused_rounds_ms": [round(x, 4) for x in fused_r], "sequential_rounds_ms": [round(x, 4) for x in seq_r],
         "seq_gemm_only_ms": round(sgwin, 4) if sgwin else None,
         "seq_gemm_only_tflops": round(flops / (sgwin * 1e-3) / 1e12, 2) if sgwin else None,
         "seq_comm_only_ms": round(scwin, 4) if scwin else None,
@@ -235,36 +256,173 @@ def measure(name, steps, warmup, sweep, fixed_wgs=0):
         res["two_stream_ms"] = two
         res["two_stream_best_ms"] = min(two.values())
     res["mfma_frac"] = round(res["kernel_tflops"] / PEAK_FP16_TFLOPS, 4)
-    if res["comm_gbps"]:
+    if clock_mhz > 0:
+        # the same work against the peak at the clock the chip held
+        res["mfma_frac_at_clock"] = round(res["kernel_tflops"] / (PEAK_FP16_TFLOPS * clock_mhz / 2400.0), 4)
+    if hbm_sized and res["comm_gbps"]:
         res["comm_hbm_frac"] = round(res["comm_gbps"] / PEAK_HBM_GBPS, 4)
-    if res["seq_comm_only_gbps"]:
+    if hbm_sized and res["seq_comm_only_gbps"]:
         res["seq_comm_only_hbm_frac"] = round(res["seq_comm_only_gbps"] / PEAK_HBM_GBPS, 4)
+    if res["seq_comm_only_cold_gbps"]:
+        res["seq_comm_only_cold_hbm_frac"] = round(res["seq_comm_only_cold_gbps"] / PEAK_HBM_GBPS, 4)
     return res, case
 
 
-def cpu_baseline(case):
-    """The oracle on the full headline problem; returns the report and the
-    number of output elements outside tolerance when compared to the GPU."""
+# ----------------------------------------------------------- oracle checks
+# Outside every timed region. Each returns (report dict, ok).
+
+def _tile_checks(C, tiles, ref_fn):
+    """Elements outside |d| <= 1e-2 + 1e-2 |ref| over the given 128x128 tiles."""
+    import numpy as np
+    bad = 0
+    M, N = C.shape
+    for (r0, c0) in tiles:
+        r1, c1 = min(M, r0 + 128), min(N, c0 + 128)
+        got = C[r0:r1, c0:c1].float().cpu().numpy().astype(np.float64)
+        ref = ref_fn(r0, r1, c0, c1)
+        bad += int((~(np.abs(got - ref) <= 1e-2 + 1e-2 * np.abs(ref))).sum())
+    return bad
+
+
+def _gathered_exact(case, chunk_rows=16384):
     import numpy as np
     import oracle
-    w = case.w
-    threads = min(16, len(os.sched_getaffinity(0)))
-    shards = [s.cpu().numpy() for s in case.inp["shards"]]
-    B = case.inp["B"].cpu().numpy()
-    bias = case.inp["bias"].cpu().numpy()
-    log(f"[cpu_baseline] oracle all_gather_matmul {w.M}x{w.N}x{w.K} on {threads} threads")
+    G, shards = case.G, case.inp["shards"]
+    for r0 in range(0, G.shape[0], chunk_rows):
+        r1 = min(G.shape[0], r0 + chunk_rows)
+        ref = oracle.all_gather_k([s[r0:r1].cpu().numpy() for s in shards])
+        if not np.array_equal(G[r0:r1].cpu().numpy().view(np.uint16), ref):
+            return False
+    return True
+
+
+def _ag_tile_ref(case):
+    import oracle
+    inp, B_cols = case.inp, {}
+
+    def ref(r0, r1, c0, c1):
+        if c0 not in B_cols:
+            B_cols[c0] = inp["B"][:, c0:c1].contiguous().cpu().numpy()
+        return oracle.all_gather_matmul([s[r0:r1].cpu().numpy() for s in inp["shards"]], B_cols[c0],
+                                        inp["bias"][c0:c1].cpu().numpy())
+    return ref
+
+
+def oracle_check(case):
+    """Checks the fused op's last outputs against the oracle: copies bit for
+    bit, floating-point outputs within 1e-2 + 1e-2 |ref|."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+    w, inp = case.w, case.inp
     t0 = time.perf_counter()
-    ref = oracle.all_gather_matmul(shards, B, bias, nthreads=threads)
-    dt = time.perf_counter() - t0
-    got = case.C.float().cpu().numpy().astype(np.float64)
-    bad = int((~(np.abs(got - ref) <= 1e-2 + 1e-2 * np.abs(ref))).sum())
-    gathered_ok = bool(np.array_equal(oracle.all_gather_k(shards), case.G.cpu().numpy().view(np.uint16)))
+    rep = {}
+    if w.op == "ag_mm":
+        if w.gemm_flops <= 2 ** 38:  # pow2_4k: the whole C
+            full = oracle.all_gather_matmul([s.cpu().numpy() for s in inp["shards"]], inp["B"].cpu().numpy(),
+                                            inp["bias"].cpu().numpy())
+            got = case.C.float().cpu().numpy().astype(np.float64)
+            rep["C_outside_tol"] = int((~(np.abs(got - full) <= 1e-2 + 1e-2 * np.abs(full))).sum())
+            rep["C_checked"] = "all"
+        else:
+            tiles = wl.sample_tiles(w.M, w.N, 128, 64, seed=0)
+            rep["C_outside_tol"] = _tile_checks(case.C, tiles, _ag_tile_ref(case))
+            rep["C_checked"] = f"{len(tiles)} sampled 128x128 tiles"
+        rep["gathered_bit_exact"] = _gathered_exact(case)
+        ok = rep["C_outside_tol"] == 0 and rep["gathered_bit_exact"]
+    elif w.op == "mm_rs":
+        A, B, bias = inp["A"].cpu().numpy(), inp["B"].cpu().numpy(), inp["bias"].cpu().numpy()
+        ref = oracle.matmul_reduce_scatter(A, B, [p.cpu().numpy() for p in inp["partials"]], w.W, rank=w.rank,
+                                           bias=bias)
+        got = case.out.float().cpu().numpy().astype(np.float64)
+        rep["out_outside_tol"] = int((~(np.abs(got - ref) <= 1e-2 + 1e-2 * np.abs(ref))).sum())
+        tiles = wl.sample_tiles(w.M, w.N, 128, 16, seed=0)
+        rep["C_outside_tol"] = _tile_checks(
+            case.C, tiles, lambda r0, r1, c0, c1: oracle.gemm_bias(A, B, bias, rows=(r0, r1), cols=(c0, c1)))
+        rep["C_checked"] = f"{len(tiles)} sampled 128x128 tiles; out: all"
+        ok = rep["out_outside_tol"] == 0 and rep["C_outside_tol"] == 0
+    else:
+        ref = oracle.all_reduce([x.cpu().numpy() for x in inp["comm_in"]])
+        got = case.out.float().cpu().numpy().astype(np.float64)
+        rep["all_reduce_outside_tol"] = int((~(np.abs(got - ref) <= 1e-2 + 1e-2 * np.abs(ref))).sum())
+        B, bias = inp["B"].cpu().numpy(), inp["bias"].cpu().numpy()
+        tiles = wl.sample_tiles(w.M, w.N, 128, 16, seed=0)
+        rep["C_outside_tol"] = _tile_checks(
+            case.C, tiles,
+            lambda r0, r1, c0, c1: oracle.gemm_bias(inp["A"][r0:r1].cpu().numpy(), B, bias, cols=(c0, c1)))
+        rep["C_checked"] = f"{len(tiles)} sampled 128x128 tiles; all_reduce: all"
+        ok = rep["all_reduce_outside_tol"] == 0 and rep["C_outside_tol"] == 0
+    rep["seconds"] = round(time.perf_counter() - t0, 2)
+    rep["ok"] = ok
+    return rep, ok
+
+
+def cpu_baseline(case):
+    """The oracle on a bounded sample of the headline all_gather_matmul:
+    CPU_TILES sampled 128x128 output tiles (fp64 dot products over the whole
+    K, plus bias) and the whole gathered buffer, on the CPU share of one GPU.
+    Returns the report and whether the GPU output agreed."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+    w, inp = case.w, case.inp
+    threads = oracle.cpu_share()
+    tiles = wl.sample_tiles(w.M, w.N, 128, CPU_TILES, seed=1)
+    # operands of the sampled tiles, on the host before the clock starts
+    rows = sorted({r0 for r0, _ in tiles})
+    cols = sorted({c0 for _, c0 in tiles})
+    A_rows = {r0: [s[r0:r0 + 128].cpu().numpy() for s in inp["shards"]] for r0 in rows}
+    B_cols = {c0: inp["B"][:, c0:c0 + 128].contiguous().cpu().numpy() for c0 in cols}
+    bias = inp["bias"].cpu().numpy()
+    shards = [s.cpu().numpy() for s in inp["shards"]]
+    log(f"[cpu_baseline] oracle: {len(tiles)} tiles of {w.name} C (K={w.K}) and the full gathered buffer "
+        f"on {threads} threads")
+    refs = {}
+    t0 = time.perf_counter()
+    for (r0, c0) in tiles:
+        refs[(r0, c0)] = oracle.all_gather_matmul(A_rows[r0], B_cols[c0], bias[c0:c0 + 128], nthreads=threads)
+    t_gemm = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    gathered = oracle.all_gather_k(shards)
+    t_gather = time.perf_counter() - t1
+    dt = t_gemm + t_gather
+    flops = 2 * 128 * 128 * w.K * len(tiles)
+    gather_bytes = 4 * w.M * w.K
+    bad = 0
+    for (r0, c0), ref in refs.items():
+        got = case.C[r0:r0 + 128, c0:c0 + 128].float().cpu().numpy().astype(np.float64)
+        bad += int((~(np.abs(got - ref) <= 1e-2 + 1e-2 * np.abs(ref))).sum())
+    gathered_ok = bool(np.array_equal(gathered, case.G.cpu().numpy().view(np.uint16)))
+    full_s = w.gemm_flops / (flops / t_gemm) + (4 * w.M * w.K) / (gather_bytes / t_gather)
     return {
-        "value": round(w.gemm_flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-        "sample": f"full {w.name} all_gather_matmul (gather + {w.M}x{w.N}x{w.K} GEMM + bias, fp64), "
-                  f"{dt:.1f} s",
+        "value": round(flops / t_gemm / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"{len(tiles)} sampled 128x128 tiles of {w.name} all_gather_matmul C (fp64 dot products over "
+                  f"K={w.K} + bias, {flops / 1e9:.1f} GFLOP, {t_gemm:.1f} s) and the full gathered buffer "
+                  f"({gather_bytes / 2**30:.0f} GiB moved, {t_gather:.1f} s); cores = the CPU share of one GPU",
         "seconds": round(dt, 2),
+        "gather_gbps": round(gather_bytes / t_gather / 1e9, 2),
+        "full_problem_s_extrapolated": round(full_s, 1),
     }, bad, gathered_ok
+
+
+def copy_ceiling():
+    """GB/s of a plain 1 GiB device-to-device copy (read + write bytes)."""
+    import torch
+    n = 1 << 29
+    src = torch.ones(n, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return round(2 * 2 * n / (ms * 1e-3) / 1e9, 1)
 
 
 def strip_comments(src):
@@ -299,14 +457,19 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def traffic_file(workload):
+    return os.path.join(PROFILES, f"persistent_kernel_ag_{workload}_traffic.txt")
+
+
 def recorded_traffic(workload):
-    """HBM bytes per launch recorded in profiles/ for this kernel build, or None.
-    (Recorded at one gemm_wgs; the split moves work between queues but not the
-    bytes the launch moves.)"""
-    if not os.path.exists(TRAFFIC_FILE):
+    """Bytes per launch fetched from beyond L2 plus written, recorded in
+    profiles/ for this kernel build, or None. (Recorded at one gemm_wgs; the
+    split moves work between queues but not the bytes the op must move.)"""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
@@ -342,26 +505,39 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(1)
+    failures = []
     head, case = measure(args.workload, args.steps, args.warmup, not args.no_sweep, args.gemm_wgs)
     cpu = None
-    if not args.no_cpu_baseline and case.w.op == "ag_mm" and case.w.gemm_flops <= 2 ** 38:
+    if not args.no_check:
+        log(f"[{args.workload}] oracle check")
+        head["oracle_check"], ok = oracle_check(case)
+        if not ok:
+            failures.append(args.workload)
+    if not args.no_cpu_baseline and case.w.op == "ag_mm":
         cpu, bad, gathered_ok = cpu_baseline(case)
-        head["oracle_check"] = {"C_outside_tol": bad, "gathered_bit_exact": gathered_ok}
+        cpu["C_outside_tol"], cpu["gathered_bit_exact"] = bad, gathered_ok
         if bad or not gathered_ok:
-            log(f"ERROR: GPU output disagrees with the oracle ({bad} elements, gathered {gathered_ok})")
+            failures.append(f"{args.workload} (cpu_baseline sample)")
     del case
     torch.cuda.empty_cache()
+    ceiling = copy_ceiling()
     extra = []
     if not args.headline_only:
-        for name in ("llama7b_gate", "concurrent", "g2"):
+        for name in EXTRA_WORKLOADS + ("g2",):
             if name == args.workload:
                 continue
             steps = 5 if name == "g2" else max(5, args.steps // 2)
             r, c = measure(name, steps, 2, not args.no_sweep)
+            if not args.no_check:
+                log(f"[{name}] oracle check")
+                r["oracle_check"], ok = oracle_check(c)
+                if not ok:
+                    failures.append(name)
             extra.append(r)
             del c
             torch.cuda.empty_cache()
     w = head
+    wl_name = "all_gather_matmul" if w["op"] == "ag_mm" else w["op"]
     line = {
         "metric": "GEMM TFLOP/s + comm-tile GB/s on 1 MI355X, as fraction of MFMA/HBM peak",
         "value": w["tflops"],
@@ -376,32 +552,42 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {
-            "workload": f"{w['workload']} {'all_gather_matmul' if w['op'] == 'ag_mm' else w['op']} local share "
-                        f"(W={w['W']}, M={w['M']}, N={w['N']}, K={w['K']})",
+            "workload": f"{w['workload']} {wl_name} local share (W={w['W']}, M={w['M']}, N={w['N']}, K={w['K']})",
             "mode": "fused", "tile": w["tile"], "gemm_wgs": w["gemm_wgs"], "grid": w["grid"],
             "accumulate": "f32",
         },
         "roofline": {
             "bound": "mfma", "achieved": w["kernel_tflops"], "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
             "frac": w["mfma_frac"], "traffic": recorded_traffic(w["workload"]),
+            "traffic_note": "bytes fetched from beyond L2 (HBM and last-level cache hits) plus bytes written, "
+                            "per launch, rocprofv3 FETCH_SIZE/WRITE_SIZE scaled by a plain copy; "
+                            f"profiles/{os.path.basename(traffic_file(w['workload']))}",
             "kernel": f"persistent_kernel<1,256,256> (fused {w['op']}), HIP-event mean over {args.steps} "
                       f"back-to-back launches: {w['kernel_ms']} ms",
+            "clock_mhz": w["clock_mhz"], "frac_at_clock": w.get("mfma_frac_at_clock"),
         },
         "comm": {
             "gbps": w["comm_gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": w.get("comm_hbm_frac"),
             "window_ms": w["comm_window_ms"], "bytes": w["comm_bytes"],
             "comm_only_gbps": w["seq_comm_only_gbps"], "comm_only_frac": w.get("seq_comm_only_hbm_frac"),
             "comm_only_cold_gbps": w["seq_comm_only_cold_gbps"],
-            "note": "gbps: fused comm window; comm_only: sequential comm kernel over all CUs, inputs left in "
-                    "the last-level cache by the previous step (warm) or flushed by a 512 MiB write (cold)",
+            "copy_ceiling_gbps": ceiling,
+            "note": "gbps: fused comm window (per-workgroup stamps); comm_only: the sequential comm kernel over "
+                    "all CUs, inputs left cached by the previous step (warm) or after a 512 MiB write (cold); "
+                    "copy_ceiling: torch device-to-device copy of 1 GiB (read + write bytes)",
         },
         "sequential_ms": w["sequential_ms"],
+        "fused_vs_sequential_ms": w["fused_vs_sequential_ms"],
         "fused_le_sequential": w["fused_le_sequential"],
+        "oracle_check": w.get("oracle_check"),
         "cpu_baseline": cpu,
         "detail": head,
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
+    if failures:
+        log(f"ERROR: the GPU output disagrees with the oracle on: {', '.join(failures)}")
+        sys.exit(1)
 
 
 if __name__ == "__main__":

@@ -100,7 +100,8 @@ class _DeviceInfo(ctypes.Structure):
     _fields_ = [("device", ctypes.c_int32), ("compute_units", ctypes.c_int32),
                 ("clock_khz", ctypes.c_int32), ("memory_clock_khz", ctypes.c_int32),
                 ("lds_bytes_per_cu", ctypes.c_int32), ("global_mem_bytes", ctypes.c_int64),
-                ("arch", ctypes.c_char * 64)]
+                ("arch", ctypes.c_char * 64), ("peak_fp16_tflops", ctypes.c_double),
+                ("peak_hbm_gbps", ctypes.c_double)]
 
 
 def _load() -> ctypes.CDLL:
@@ -124,6 +125,8 @@ def _load() -> ctypes.CDLL:
                                   ctypes.POINTER(_PredictParams), ctypes.POINTER(ctypes.c_float),
                                   ctypes.POINTER(i32)],
         "iris_last_windows": [vp, vp] + [ctypes.POINTER(ctypes.c_double)] * 4,
+        "iris_check_device_error": [vp, vp],
+        "iris_last_clock": [vp, vp, ctypes.POINTER(ctypes.c_double)],
         "iris_device_info": [i32, ctypes.POINTER(_DeviceInfo)],
         "iris_status_str": [i32],
         "iris_last_error_message": [],
@@ -194,9 +197,102 @@ def _ws(workspace: Optional[torch.Tensor]):
 
 
 def _shape2(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
     if t.dim() != 2:
         raise ValueError(f"{name} must be 2-D")
     return t.shape
+
+
+# Shape checks. They run before any pointer is taken: a tensor whose shape
+# does not match the M, N, K, W the library derives would be read or written
+# past its end by the kernels.
+
+def _want_shape(t, shape, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _want_numel(t, n: int, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.numel() != n:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+
+
+def _want_count(ts, n: int, name: str) -> None:
+    if len(ts) != n:
+        raise ValueError(f"{name} holds {len(ts)} tensors, expected {n}")
+
+
+def _bias_along_m(config) -> bool:
+    if config is None:
+        return False
+    flags = config.get("flags", 0) if isinstance(config, dict) else config.flags
+    return bool(int(flags) & IRIS_FLAG_BIAS_ALONG_M)
+
+
+def _want_bias(bias, M: int, N: int, config) -> None:
+    if bias is not None:
+        _want_numel(bias, M if _bias_along_m(config) else N, "bias")
+
+
+def _want_w(W: int) -> None:
+    if not 1 <= int(W) <= IRIS_MAX_W:
+        raise ValueError(f"W must be in [1, {IRIS_MAX_W}] (got {W})")
+
+
+def _validate(op, config, C=None, out=None, A=None, srcs=(), W=1, B=None, bias=None, M=0, N=0, K=0,
+              comm_elems=0, collective=IRIS_COLL_ALL_REDUCE):
+    """Checks every tensor of op `op` against the shape the library derives
+    (K is K_local for all_gather_matmul)."""
+    _want_w(W)
+    if op == IRIS_OP_AG_MM:
+        _want_count(srcs, W, "A_shards")
+        for s, t in enumerate(srcs):
+            _want_shape(t, (M, K), f"A_shards[{s}]")
+        _want_shape(B, (W * K, N), "B")
+        _want_shape(C, (M, N), "C")
+        _want_shape(out, (M, W * K), "A_gathered")
+    elif op in (IRIS_OP_MM_RS, IRIS_OP_MM_AR):
+        if op == IRIS_OP_MM_RS and N % W != 0:
+            raise ValueError(f"N ({N}) must be divisible by W ({W})")
+        cols = N // W if op == IRIS_OP_MM_RS else N
+        _want_shape(A, (M, K), "A")
+        _want_shape(B, (K, N), "B")
+        _want_shape(C, (M, N), "C")
+        _want_shape(out, (M, cols), "out")
+        _want_count(srcs, W - 1, "partials")
+        for p, t in enumerate(srcs):
+            _want_shape(t, (M, cols), f"partials[{p}]")
+    elif op == IRIS_OP_CONCURRENT:
+        _want_shape(A, (M, K), "A")
+        _want_shape(B, (K, N), "B")
+        _want_shape(C, (M, N), "C")
+        _want_count(srcs, W, "comm_in")
+        for w, t in enumerate(srcs):
+            _want_numel(t, comm_elems, f"comm_in[{w}]")
+        if collective in _COMM_OUT_LEN:
+            _want_numel(out, _COMM_OUT_LEN[collective](comm_elems, W), "comm_out")
+    elif op == IRIS_OP_MM_AG:
+        _want_shape(A, (M, K), "A")
+        _want_shape(B, (K, N), "B")
+        _want_shape(out, (M * W, N), "out")
+        _want_count(srcs, W - 1, "peers")
+        for p, t in enumerate(srcs):
+            _want_shape(t, (M, N), f"peers[{p}]")
+    else:
+        raise ValueError(f"unknown op {op}")
+    _want_bias(bias, M, N, config)
+
+
+_COMM_OUT_LEN = {
+    IRIS_COLL_ALL_REDUCE: lambda n, W: n, IRIS_COLL_ALL_GATHER: lambda n, W: W * n,
+    IRIS_COLL_REDUCE_SCATTER: lambda n, W: n // W, IRIS_COLL_ALL_TO_ALL: lambda n, W: n,
+    IRIS_COLL_BROADCAST: lambda n, W: n,
+}
 
 
 # ----------------------------------------------------------------------- ops
@@ -204,8 +300,12 @@ def _shape2(t: torch.Tensor, name: str):
 def iris_ag_mm(C, A_gathered, A_shards, B, bias=None, config=None, workspace=None, stream=None):
     """all_gather_matmul local share: A_gathered = concat_K(A_shards); C = A_gathered @ B + bias."""
     W = len(A_shards)
+    if W < 1:
+        raise ValueError("A_shards is empty")
     M, K_local = _shape2(A_shards[0], "A_shards[0]")
     N = _shape2(B, "B")[1]
+    _validate(IRIS_OP_AG_MM, config, C=C, out=A_gathered, srcs=A_shards, W=W, B=B, bias=bias, M=M, N=N,
+              K=K_local)
     ws, wsb = _ws(workspace)
     _check(_lib.iris_ag_mm(_ptr(C, "C"), _ptr(A_gathered, "A_gathered"), _ptr_array(A_shards, "A_shards"),
                            W, _ptr(B, "B"), _ptr(bias, "bias", True), M, N, K_local, _cfg(config),
@@ -217,6 +317,7 @@ def iris_mm_rs_local(out, C, A, B, partials, W, rank=0, bias=None, config=None, 
     """matmul_reduce_scatter local share: C = A @ B + bias; out = C[:, rank*N/W:(rank+1)*N/W] + sum(partials)."""
     M, K = _shape2(A, "A")
     N = _shape2(B, "B")[1]
+    _validate(IRIS_OP_MM_RS, config, C=C, out=out, A=A, srcs=partials, W=W, B=B, bias=bias, M=M, N=N, K=K)
     ws, wsb = _ws(workspace)
     _check(_lib.iris_mm_rs_local(_ptr(out, "out"), _ptr(C, "C"), _ptr(A, "A"), _ptr(B, "B"),
                                  _ptr(bias, "bias", True), _ptr_array(partials, "partials"), W, rank,
@@ -227,17 +328,11 @@ def iris_mm_ar_local(out, C, A, B, partials, W, bias=None, config=None, workspac
     """matmul_all_reduce local share: C = A @ B + bias; out = C + sum(partials)."""
     M, K = _shape2(A, "A")
     N = _shape2(B, "B")[1]
+    _validate(IRIS_OP_MM_AR, config, C=C, out=out, A=A, srcs=partials, W=W, B=B, bias=bias, M=M, N=N, K=K)
     ws, wsb = _ws(workspace)
     _check(_lib.iris_mm_ar_local(_ptr(out, "out"), _ptr(C, "C"), _ptr(A, "A"), _ptr(B, "B"),
                                  _ptr(bias, "bias", True), _ptr_array(partials, "partials"), W,
                                  M, N, K, _cfg(config), ws, wsb, _stream(stream)))
-
-
-_COMM_OUT_LEN = {
-    IRIS_COLL_ALL_REDUCE: lambda n, W: n, IRIS_COLL_ALL_GATHER: lambda n, W: W * n,
-    IRIS_COLL_REDUCE_SCATTER: lambda n, W: n // W, IRIS_COLL_ALL_TO_ALL: lambda n, W: n,
-    IRIS_COLL_BROADCAST: lambda n, W: n,
-}
 
 
 def iris_concurrent(C, A, B, comm_out, comm_in, bias=None, collective=IRIS_COLL_ALL_REDUCE, rank=0,
@@ -247,11 +342,12 @@ def iris_concurrent(C, A, B, comm_out, comm_in, bias=None, collective=IRIS_COLL_
     comm_out; `rank` is this rank (the root for broadcast)."""
     M, K = _shape2(A, "A")
     N = _shape2(B, "B")[1]
-    n = comm_in[0].numel()
     W = len(comm_in)
-    if collective in _COMM_OUT_LEN and comm_out.numel() != _COMM_OUT_LEN[collective](n, W):
-        raise ValueError(f"comm_out has {comm_out.numel()} elements, collective {collective} of {W} "
-                         f"buffers of {n} writes {_COMM_OUT_LEN[collective](n, W)}")
+    if W < 1:
+        raise ValueError("comm_in is empty")
+    n = comm_in[0].numel()
+    _validate(IRIS_OP_CONCURRENT, config, C=C, out=comm_out, A=A, srcs=comm_in, W=W, B=B, bias=bias, M=M, N=N,
+              K=K, comm_elems=n, collective=collective)
     ws, wsb = _ws(workspace)
     _check(_lib.iris_concurrent(_ptr(C, "C"), _ptr(A, "A"), _ptr(B, "B"), _ptr(bias, "bias", True),
                                 M, N, K, collective, rank, _ptr(comm_out, "comm_out"),
@@ -264,8 +360,7 @@ def iris_mm_ag_local(out, A, B, peers, W, rank=0, bias=None, config=None, worksp
     along M; this rank's block is computed, the W-1 `peers` (M, N) are copied."""
     M, K = _shape2(A, "A")
     N = _shape2(B, "B")[1]
-    if out.numel() != M * W * N:
-        raise ValueError(f"out has {out.numel()} elements, expected {M * W} x {N}")
+    _validate(IRIS_OP_MM_AG, config, out=out, A=A, srcs=peers, W=W, B=B, bias=bias, M=M, N=N, K=K)
     ws, wsb = _ws(workspace)
     _check(_lib.iris_mm_ag_local(_ptr(out, "out"), _ptr(A, "A"), _ptr(B, "B"), _ptr(bias, "bias", True),
                                  _ptr_array(peers, "peers"), W, rank, M, N, K, _cfg(config), ws, wsb,
@@ -308,6 +403,8 @@ def iris_tune_gemm_wgs(op, candidates, reps=5, config=None, stream=None, *, top_
     """Sweep gemm_wgs over `candidates` (the static default is always added),
     cache and return (best, {candidate: median ms}). With top_k > 0 only the
     top_k candidates the predictor ranks best are run (the others read -1)."""
+    _validate(op, config, C=C, out=out, A=A, srcs=srcs, W=W, B=B, bias=bias, M=M, N=N, K=K,
+              comm_elems=comm_elems, collective=collective or IRIS_COLL_ALL_REDUCE)
     a, keep = _op_args(op, config, C, out, A, srcs, W, rank, collective, B, bias, M, N, K, comm_elems)
     cands = (ctypes.c_int32 * max(1, len(candidates)))(*candidates)
     ms = (ctypes.c_float * max(1, len(candidates)))()
@@ -346,6 +443,23 @@ def iris_last_windows(workspace=None, stream=None):
     ws, _ = _ws(workspace)
     _check(_lib.iris_last_windows(ws, _stream(stream), *[ctypes.byref(v) for v in vals]))
     return tuple(v.value for v in vals)
+
+
+def iris_last_clock(workspace=None, stream=None) -> float:
+    """Shader clock (MHz) held during the last persistent launch on this
+    workspace (-1 if none was recorded)."""
+    v = ctypes.c_double()
+    ws, _ = _ws(workspace)
+    _check(_lib.iris_last_clock(ws, _stream(stream), ctypes.byref(v)))
+    return v.value
+
+
+def iris_check_device_error(workspace=None, stream=None) -> None:
+    """Waits for the stream; raises IrisError (IRIS_ERR_DEVICE_TIMEOUT) if a
+    device-side wait of a fused op on this workspace gave up since the last
+    check (the outputs of those ops are then not to be trusted)."""
+    ws, _ = _ws(workspace)
+    _check(_lib.iris_check_device_error(ws, _stream(stream)))
 
 
 def iris_device_info(device: int = 0) -> dict:

@@ -105,7 +105,7 @@ std::string cache_path() {
   const char* p = getenv("IRIS_LOCAL_TUNE_CACHE");
   if (p && *p) return p;
   const char* home = getenv("HOME");
-  return std::string(home && *home ? home : "/tmp") + "/.cache/iris_local/tune.txt";
+  return std::string(home && *home ? home : "/tmp") + "/.cache/iris_local/tune.json";
 }
 
 std::string cache_key(const std::string& arch, int op, int64_t M, int64_t N, int64_t K, int W, int bm,
@@ -117,21 +117,84 @@ std::string cache_key(const std::string& arch, int op, int64_t M, int64_t N, int
   return buf;
 }
 
-std::map<std::string, int> load_cache() {
-  std::map<std::string, int> db;
-  FILE* f = fopen(cache_path().c_str(), "r");
-  if (!f) return db;
-  char line[512];
-  while (fgets(line, sizeof line, f)) {
-    char* eq = strrchr(line, '=');
-    if (!eq) continue;
-    *eq = 0;
-    std::string key(line);
-    while (!key.empty() && key.back() == ' ') key.pop_back();
-    db[key] = atoi(eq + 1);
+// The cache is one JSON object mapping a key string to the tuned gemm_wgs,
+// e.g. {"gfx950 op1 M4096 N4096 K512 W8 t256x256x64 g8": 1}. The reader
+// accepts exactly that shape (string keys with \" and \\ escapes, integer
+// values, any white space); a file it cannot parse is treated as empty.
+struct JsonIn {
+  const std::string& s;
+  size_t i = 0;
+  void ws() {
+    while (i < s.size() && (s[i] == ' ' || s[i] == '\n' || s[i] == '\t' || s[i] == '\r')) ++i;
   }
-  fclose(f);
+  bool eat(char c) {
+    ws();
+    if (i < s.size() && s[i] == c) {
+      ++i;
+      return true;
+    }
+    return false;
+  }
+  bool str(std::string* out) {
+    if (!eat('"')) return false;
+    out->clear();
+    while (i < s.size() && s[i] != '"') {
+      char c = s[i++];
+      if (c == '\\') {
+        if (i >= s.size()) return false;
+        c = s[i++];
+        if (c != '"' && c != '\\' && c != '/') return false;
+      }
+      out->push_back(c);
+    }
+    return eat('"');
+  }
+  bool integer(long* out) {
+    ws();
+    const char* b = s.c_str() + i;
+    char* e = nullptr;
+    errno = 0;
+    const long v = strtol(b, &e, 10);
+    if (e == b || errno != 0) return false;
+    i += (size_t)(e - b);
+    *out = v;
+    return true;
+  }
+};
+
+std::map<std::string, int> parse_cache(const std::string& text) {
+  std::map<std::string, int> db;
+  JsonIn in{text};
+  if (!in.eat('{')) return {};
+  if (in.eat('}')) return db;
+  do {
+    std::string k;
+    long v = 0;
+    if (!in.str(&k) || !in.eat(':') || !in.integer(&v)) return {};
+    if (v > 0 && v < (1 << 20)) db[k] = (int)v;
+  } while (in.eat(','));
+  if (!in.eat('}')) return {};
   return db;
+}
+
+std::map<std::string, int> load_cache() {
+  FILE* f = fopen(cache_path().c_str(), "r");
+  if (!f) return {};
+  std::string text;
+  char buf[4096];
+  size_t n;
+  while ((n = fread(buf, 1, sizeof buf, f)) > 0) text.append(buf, n);
+  fclose(f);
+  return parse_cache(text);
+}
+
+std::string json_escape(const std::string& k) {
+  std::string o;
+  for (char c : k) {
+    if (c == '"' || c == '\\') o.push_back('\\');
+    o.push_back(c);
+  }
+  return o;
 }
 
 void mkdirs(const std::string& path) {
@@ -147,8 +210,12 @@ void save_cache_entry(const std::string& key, int value) {
   const std::string tmp = path + "." + std::to_string(getpid()) + ".tmp";
   FILE* f = fopen(tmp.c_str(), "w");
   if (!f) return;  // an unwritable cache only loses the memo
-  bool ok = true;
-  for (auto& kv : db) ok = ok && fprintf(f, "%s = %d\n", kv.first.c_str(), kv.second) > 0;
+  bool ok = fputs("{\n", f) >= 0;
+  size_t i = 0;
+  for (auto& kv : db)
+    ok = ok && fprintf(f, "  \"%s\": %d%s\n", json_escape(kv.first).c_str(), kv.second,
+                       ++i < db.size() ? "," : "") > 0;
+  ok = ok && fputs("}\n", f) >= 0;
   ok = (fclose(f) == 0) && ok;
   if (!ok || rename(tmp.c_str(), path.c_str()) != 0) unlink(tmp.c_str());
 }
@@ -262,7 +329,7 @@ int default_comm_rows(int kind, int bm, int64_t row_bytes) {
 
 // ------------------------------------------------------------- workspace
 constexpr int kMaxGrid = iris::kMaxGrid;
-constexpr size_t kStampBytes = (size_t)kMaxGrid * 6 * sizeof(uint64_t);
+constexpr size_t kStampBytes = (size_t)kMaxGrid * iris::kStampWords * sizeof(uint64_t);
 
 int64_t flag_words(int kind, int64_t M, int64_t N, int W, int bm, int bn) {
   const int64_t n_pm = (M + bm - 1) / bm, n_pn = (N + bn - 1) / bn;
@@ -391,6 +458,25 @@ int get_side_stream(int dev, void* stream, SideStream** out) {
   }
   *out = &ss;
   return IRIS_OK;
+}
+
+// Waits for `stream`, then reads and clears the status word of workspace
+// `ws`: the timeout bit is set by the last workgroup of any fused launch in
+// which a device-side wait gave up, and stays set until read here.
+int read_status(void* ws, hipStream_t s) {
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  int32_t* word = (int32_t*)((char*)ws + kStampBytes) + iris::kStatus;
+  int32_t v = 0;
+  e = hipMemcpy(&v, word, 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "status readback");
+  if (v == 0) return IRIS_OK;
+  e = hipMemset(word, 0, 4);
+  if (e != hipSuccess) return hip_fail(e, "status clear");
+  e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "status clear");
+  return fail(IRIS_ERR_DEVICE_TIMEOUT, "a device-side wait hit its poll bound; the outputs of the ops since the "
+              "last check are not to be trusted");
 }
 
 int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_bytes, void* stream,
@@ -598,17 +684,7 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
     std::lock_guard<std::mutex> lk(g_mu);
     g_last[ws] = LastLaunch{dev, gemm_grid, comm_grid, r.mode == IRIS_MODE_FUSED, 0};
   }
-  if (getenv("IRIS_LOCAL_DEBUG")) {
-    e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return hip_fail(e, "debug sync");
-    int32_t err = 0;
-    e = hipMemcpy(&err, p.ws + iris::kErr, 4, hipMemcpyDeviceToHost);
-    if (e != hipSuccess) return hip_fail(e, "debug readback");
-    if (err) {
-      (void)hipMemset(p.ws + iris::kErr, 0, 4);
-      return fail(IRIS_ERR_DEVICE_TIMEOUT, "a device-side wait hit its poll bound");
-    }
-  }
+  if (getenv("IRIS_LOCAL_DEBUG")) return read_status(ws, s);
   return IRIS_OK;
 }
 
@@ -980,7 +1056,7 @@ int iris_last_windows(void* workspace, void* stream, double* gs_ns, double* ge_n
   }
   e = hipStreamSynchronize((hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-  std::vector<uint64_t> st((size_t)kMaxGrid * 6);
+  std::vector<uint64_t> st((size_t)kMaxGrid * iris::kStampWords);
   e = hipMemcpy(st.data(), (char*)ws + last.stamp_off, st.size() * 8, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "stamp readback");
   DevInfo di;
@@ -1007,6 +1083,65 @@ int iris_last_windows(void* workspace, void* stream, double* gs_ns, double* ge_n
   return IRIS_OK;
 }
 
+int iris_last_clock(void* workspace, void* stream, double* mhz) {
+  g_msg.clear();
+  if (!mhz) return fail(IRIS_ERR_INVALID_ARG, "mhz is NULL");
+  *mhz = -1.0;
+  void* ws = workspace;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  LastLaunch last;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!ws) {
+      auto it = g_ws.find({dev, stream});
+      if (it == g_ws.end()) return fail(IRIS_ERR_INVALID_ARG, "no library workspace for this stream yet");
+      ws = it->second.ptr;
+    }
+    auto lt = g_last.find(ws);
+    if (lt == g_last.end()) return fail(IRIS_ERR_INVALID_ARG, "no launch recorded for this workspace");
+    last = lt->second;
+  }
+  e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  std::vector<uint64_t> ck((size_t)kMaxGrid * 4);
+  e = hipMemcpy(ck.data(), (char*)ws + last.stamp_off + (size_t)kMaxGrid * iris::kClockOff * 8, ck.size() * 8,
+                hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "clock readback");
+  DevInfo di;
+  int d2;
+  int s2 = current_device(&d2, &di);
+  if (s2) return s2;
+  double cycles = 0, ticks = 0;
+  for (int b = 0; b < last.grid; ++b) {
+    const uint64_t* w = &ck[(size_t)b * 4];
+    if (w[2] > w[0] && w[3] > w[1]) {
+      cycles += (double)(w[2] - w[0]);
+      ticks += (double)(w[3] - w[1]);
+    }
+  }
+  if (ticks > 0) *mhz = cycles / ticks * (double)di.wall_khz / 1e3;
+  return IRIS_OK;
+}
+
+int iris_check_device_error(void* workspace, void* stream) {
+  g_msg.clear();
+  void* ws = workspace;
+  if (!ws) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_ws.find({dev, stream});
+    if (it == g_ws.end() || !it->second.ptr) return IRIS_OK;  // no op has used it: nothing to report
+    ws = it->second.ptr;
+  } else if ((uintptr_t)ws % 256 != 0) {
+    return fail(IRIS_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  }
+  return read_status(ws, (hipStream_t)stream);
+}
+
 int iris_device_info(int32_t device, iris_device_info_t* info) {
   g_msg.clear();
   if (!info) return fail(IRIS_ERR_INVALID_ARG, "info is NULL");
@@ -1025,6 +1160,9 @@ int iris_device_info(int32_t device, iris_device_info_t* info) {
   info->lds_bytes_per_cu = (int32_t)prop.maxSharedMemoryPerMultiProcessor;
   info->global_mem_bytes = (int64_t)prop.totalGlobalMem;
   snprintf(info->arch, sizeof info->arch, "%s", prop.gcnArchName);
+  const bool gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  info->peak_fp16_tflops = gfx950 ? (double)prop.multiProcessorCount * prop.clockRate * 1e3 * 4096.0 / 1e12 : 0.0;
+  info->peak_hbm_gbps = gfx950 ? 8000.0 : 0.0;
   return IRIS_OK;
 }
 

@@ -356,6 +356,13 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(Params p) {
   __shared__ int slot[2];
   uint64_t gs = ~0ull, ge = 0, cs = ~0ull, ce = 0;
   bool rows_ready = false;
+  // shader-clock and constant-rate counters at entry (and exit, below): the
+  // host divides one by the other for the clock the chip held
+  __shared__ uint64_t entry[2];
+  if (threadIdx.x == 0) {
+    entry[0] = clock64();
+    entry[1] = wall_clock64();
+  }
   const int home = xcd_id();
   uint32_t gone = 0;
   const bool gemm_first = (int)blockIdx.x < p.gemm_wgs || p.T_comm == 0;
@@ -416,6 +423,11 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(Params p) {
     st[1] = ge;
     st[2] = cs;
     st[3] = ce;
+    uint64_t* ck = p.stamps + (size_t)kMaxGrid * kClockOff + (size_t)blockIdx.x * 4;
+    ck[0] = entry[0];
+    ck[1] = entry[1];
+    ck[2] = clock64();
+    ck[3] = wall_clock64();
     // Every counter and flag access of this workgroup was made by this
     // thread, at agent scope; once they have completed (the drain) none can
     // follow the count below, so the last workgroup's reset cannot race
@@ -428,8 +440,14 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(Params p) {
   }
   __syncthreads();
   if (slot[0]) {  // last workgroup out: leave the workspace zeroed for the next op
+    // every other workgroup's accesses completed before its count (above),
+    // so the error word is final here; its bit outlives the launch in the
+    // status word, which only the host clears
+    if (threadIdx.x == 0 && ld_relaxed(p.ws + kErr) != 0)
+      __hip_atomic_fetch_or(p.ws + kStatus, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
     for (int i = threadIdx.x; i < p.n_reset; i += kThreads)
-      if (i != kErr) p.ws[i] = 0;
+      if (i != kStatus) p.ws[i] = 0;
   }
 }
 

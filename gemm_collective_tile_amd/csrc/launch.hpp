@@ -22,25 +22,33 @@ enum OpKind : int32_t {
 };
 
 // Workspace layout: first uint64 stamps[kMaxGrid][4] written by the
-// persistent kernel and uint64 comm_stamps[kMaxGrid][2] written by the
-// sequential-mode comm kernel (a fixed-size block), then the int32 words
-//   GEMM queue counters (one per XCD), comm queue counter, error word (sticky), finished-
-//   workgroup counter, finished comm units (all_gather), then from kFlagBase
-//   the ready words: all_gather, one counter per GEMM row block (finished
-//   copy units of that block, kLine words apart); reduce, one flag per GEMM
-//   tile
-// Every word but the error word is zero when a persistent launch starts; the
-// last workgroup to finish zeroes them again, so consecutive ops on one
-// workspace need no separate reset.
+// persistent kernel, uint64 comm_stamps[kMaxGrid][2] written by the
+// sequential-mode comm kernel and uint64 clocks[kMaxGrid][4] (shader-clock
+// and 100 MHz counters at entry and exit of each persistent workgroup), a
+// fixed-size block of kStampWords words, then the int32 words
+//   GEMM queue counters (one per XCD), comm queue counter, error word (set
+//   by a wait that gave up during this launch), finished-workgroup counter,
+//   finished comm units (all_gather), status word, then from kFlagBase the
+//   ready words: all_gather, one counter per GEMM row block (finished copy
+//   units of that block, kLine words apart); reduce, one flag per GEMM tile
+// Every word but the status word is zero when a persistent launch starts;
+// the last workgroup to finish folds the error word into the status word and
+// zeroes the rest again, so consecutive ops on one workspace need no
+// separate reset. The status word keeps its bits until the host reads and
+// clears it (iris_check_device_error).
 // Each counter sits on its own 128-byte line (kLine words), and so does each
 // all_gather row-block counter: many workgroups poll these while others bump
 // them, and words sharing a line would serialise both.
 constexpr int kLine = 32;
 constexpr int kCtrGemm = 0;  // kXcds GEMM queue counters, one line each
 constexpr int kCtrComm = kXcds * kLine, kErr = kCtrComm + kLine, kDone = kErr + kLine,
-              kCommDone = kDone + kLine;
-constexpr int kFlagBase = kCommDone + kLine;
+              kCommDone = kDone + kLine, kStatus = kCommDone + kLine;
+constexpr int kFlagBase = kStatus + kLine;
+// bits of the status word
+constexpr int kStatusTimeout = 1;
 constexpr int kMaxGrid = 2048;
+constexpr int kClockOff = 6;    // clocks start at stamps + kMaxGrid * kClockOff
+constexpr int kStampWords = 10; // uint64 words per workgroup slot in the stamp block
 
 struct Params {
   GemmArgs g;
@@ -56,7 +64,7 @@ struct Params {
   uint64_t* stamps;          // [gridDim.x][4]: gemm start/end, comm start/end
   uint64_t* comm_stamps;     // [gridDim.x][2]: comm-only kernel start/end
   uint32_t spin_limit;       // bound on polls of one flag wait
-  int32_t n_reset;           // words [0, n_reset) (except kErr) to zero at the end
+  int32_t n_reset;           // words [0, n_reset) (except kStatus) to zero at the end
 };
 
 hipError_t launch_persistent(const Params& p, int bm, int bn, int grid, hipStream_t s);

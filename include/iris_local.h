@@ -77,12 +77,15 @@ typedef enum iris_status {
 /*
  * Every device-side wait (a GEMM tile for its gathered rows, a reduce unit
  * for its tiles) polls at most a bounded number of times, then records an
- * error word in the workspace and goes on, so every launch ends. With the
- * environment variable IRIS_LOCAL_DEBUG set, each op synchronizes its
- * stream, reads that word, and returns IRIS_ERR_DEVICE_TIMEOUT if it was
- * set (the outputs of that call are then not to be trusted).
- * IRIS_LOCAL_SPIN_LIMIT=n (n >= 0) sets the poll bound (default 2^24), so
- * that the error path can be exercised.
+ * error in the workspace and goes on, so every launch ends. The last
+ * workgroup of the launch folds that error into the workspace's status word,
+ * which keeps it until iris_check_device_error() reads and clears it. An op
+ * call itself does not wait for its kernels, so it returns IRIS_OK even when
+ * one of its waits later gives up: call iris_check_device_error() after the
+ * ops whose outputs you rely on. With the environment variable
+ * IRIS_LOCAL_DEBUG set, every op makes that check itself before returning
+ * (synchronizing its stream). IRIS_LOCAL_SPIN_LIMIT=n (n >= 0) sets the poll
+ * bound (default 2^24), so that the error path can be exercised.
  */
 
 /* execution modes ([PR544] description) */
@@ -245,11 +248,14 @@ int iris_concurrent(void* C, const void* A, const void* B, const void* bias,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace an op needs (0 on invalid arguments). The
- * workspace holds the two queue counters, the ready flags and per-workgroup
- * timestamps. A caller passing its own must give at least this much, 256-byte
- * aligned and ZERO-FILLED before its first use; every op leaves it zeroed
- * again (the last workgroup of the launch clears what the launch used), so
- * one zero fill serves any number of later ops. */
+ * workspace holds per-workgroup timestamps, then the queue counters (one
+ * GEMM queue per XCD and the comm queue), the finished-workgroup and
+ * finished-unit counters, the error and status words and the ready flags.
+ * A caller passing its own must give at least this much, 256-byte aligned
+ * and ZERO-FILLED before its first use; every op leaves it zeroed again (the
+ * last workgroup of the launch clears what the launch used) except for the
+ * status word, which only iris_check_device_error() clears, so one zero fill
+ * serves any number of later ops. */
 size_t iris_workspace_size(int32_t op, int64_t M, int64_t N, int64_t K, int32_t W,
                            const iris_config_t* cfg);
 
@@ -265,7 +271,7 @@ int iris_grid_size(int32_t op, const iris_config_t* cfg);
  * median), writes the winner to *best_gemm_wgs and the median milliseconds
  * of each candidate to ms_out[i] (may be NULL), and stores the winner in the
  * tuning cache (file named by IRIS_LOCAL_TUNE_CACHE, default
- * ~/.cache/iris_local/tune.txt; written to a temporary file then renamed;
+ * ~/.cache/iris_local/tune.json, one JSON object of key -> gemm_wgs; written to a temporary file then renamed;
  * a failed write is ignored; the file is read once per process, and this
  * process's later tunings update that copy). Blocks until done. Ties go to more GEMM
  * workgroups. The op's outputs hold the last candidate's results.
@@ -334,6 +340,33 @@ int iris_last_windows(void* workspace, void* stream, double* gemm_start_ns,
                       double* gemm_end_ns, double* comm_start_ns,
                       double* comm_end_ns);
 
+/*
+ * Shader clock (MHz) the device held during the last persistent launch that
+ * used `workspace` (NULL: the library's own workspace for `stream`): the
+ * shader-clock counter (s_memtime) over the constant-rate counter
+ * (s_memrealtime), summed over that launch's workgroups from entry to exit.
+ * Waits for `stream`. *mhz is -1 if nothing was recorded.
+ */
+int iris_last_clock(void* workspace, void* stream, double* mhz);
+
+/*
+ * Device-side errors since the last check on `workspace` (NULL: the
+ * library's own workspace for `stream`). Waits for `stream`, then returns
+ * IRIS_ERR_DEVICE_TIMEOUT (and clears the status) if a device-side wait of
+ * any fused op on that workspace gave up since the last check: the outputs
+ * of those ops are then not to be trusted. IRIS_OK otherwise, also when no
+ * op has used the library's workspace for `stream` yet.
+ */
+int iris_check_device_error(void* workspace, void* stream);
+
+/*
+ * Facts about a device, and the peak rates that roofline fractions are
+ * taken against. peak_fp16_tflops is the dense fp16 matrix rate at the
+ * maximum engine clock: CUs x clock x 4096 FLOP per CU per clock (gfx950:
+ * four matrix units per CU, each 1024 fp16 FLOP per clock; 2.5 PFLOP/s on
+ * MI355X at 2.4 GHz). peak_hbm_gbps is the published HBM3E bandwidth of the
+ * gfx950 parts (8 TB/s); 0 for a device this library does not run on.
+ */
 typedef struct iris_device_info {
   int32_t device;
   int32_t compute_units;
@@ -342,6 +375,8 @@ typedef struct iris_device_info {
   int32_t lds_bytes_per_cu;
   int64_t global_mem_bytes;
   char arch[64];             /* gcnArchName, e.g. "gfx950:sramecc+:xnack-" */
+  double peak_fp16_tflops;   /* dense fp16 MFMA peak at clock_khz */
+  double peak_hbm_gbps;      /* published HBM bandwidth, GB/s */
 } iris_device_info_t;
 
 int iris_device_info(int32_t device, iris_device_info_t* info);

@@ -74,6 +74,20 @@ def default_threads() -> int:
     return _load().oracle_default_threads()
 
 
+def cpu_share() -> int:
+    """Threads a call with nthreads=0 uses: IRIS_ORACLE_THREADS if set, else
+    the cores this process may run on, at most 16 (the CPU share of one GPU
+    on the machines the tests and the benchmark run on)."""
+    env = os.environ.get("IRIS_ORACLE_THREADS")
+    if env:
+        return max(1, int(env))
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _nt(nthreads: int) -> int:
+    return nthreads if nthreads > 0 else cpu_share()
+
+
 def _u16(a):
     """Contiguous uint16 view of an fp16/uint16 numpy array."""
     a = np.ascontiguousarray(a)
@@ -128,7 +142,7 @@ def gemm_bias(A, B, bias=None, bias_along_m=False, rows=None, cols=None, nthread
     bias = None if bias is None else _u16(bias)
     out = np.empty((m1 - m0, n1 - n0), np.float64)
     _load().oracle_gemm_bias(_p16(A), K, _p16(B), N, _p16(bias), _bias_mode(bias, bias_along_m),
-                             K, m0, m1, n0, n1, out.ctypes.data_as(_f64p), nthreads)
+                             K, m0, m1, n0, n1, out.ctypes.data_as(_f64p), _nt(nthreads))
     return out
 
 
@@ -164,7 +178,7 @@ def all_gather_matmul(shards, B, bias=None, bias_along_m=False, rows=None, cols=
     out = np.empty((m1 - m0, n1 - n0), np.float64)
     _load().oracle_all_gather_matmul(_ptr_array(shards), W, M, kl, _p16(B), N, _p16(bias),
                                      _bias_mode(bias, bias_along_m), m0, m1, n0, n1,
-                                     out.ctypes.data_as(_f64p), nthreads)
+                                     out.ctypes.data_as(_f64p), _nt(nthreads))
     return out
 
 
@@ -184,7 +198,7 @@ def matmul_reduce_scatter(A, B, partials, W, rank=0, bias=None, bias_along_m=Fal
     pp = _ptr_array(partials) if partials else None
     _load().oracle_matmul_reduce_scatter(_p16(A), _p16(B), _p16(bias),
                                          _bias_mode(bias, bias_along_m), pp, W, rank,
-                                         M, N, K, m0, m1, out.ctypes.data_as(_f64p), nthreads)
+                                         M, N, K, m0, m1, out.ctypes.data_as(_f64p), _nt(nthreads))
     return out
 
 
@@ -201,7 +215,7 @@ def matmul_all_reduce(A, B, partials, W, bias=None, bias_along_m=False, rows=Non
     out = np.empty((m1 - m0, N), np.float64)
     pp = _ptr_array(partials) if partials else None
     _load().oracle_matmul_all_reduce(_p16(A), _p16(B), _p16(bias), _bias_mode(bias, bias_along_m),
-                                     pp, W, M, N, K, m0, m1, out.ctypes.data_as(_f64p), nthreads)
+                                     pp, W, M, N, K, m0, m1, out.ctypes.data_as(_f64p), _nt(nthreads))
     return out
 
 
@@ -225,7 +239,7 @@ def matmul_all_gather(A, B, peers, W, rank=0, bias=None, bias_along_m=False, row
     out = np.empty((m1 - m0, N), np.float64)
     pp = _ptr_array(peers) if peers else None
     _load().oracle_matmul_all_gather(_p16(A), _p16(B), _p16(bias), _bias_mode(bias, bias_along_m),
-                                     pp, W, rank, M, N, K, m0, m1, out.ctypes.data_as(_f64p), nthreads)
+                                     pp, W, rank, M, N, K, m0, m1, out.ctypes.data_as(_f64p), _nt(nthreads))
     return out
 
 

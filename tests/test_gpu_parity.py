@@ -2,6 +2,8 @@
 and ragged shapes that span several tiles, plus the invariants that pin the
 schedule: bit-identical results across gemm_wgs, modes and repeats.
 """
+import json
+
 import numpy as np
 import pytest
 import torch
@@ -331,11 +333,18 @@ def test_windows_and_device_info():
     info = il.iris_device_info(0)
     note(f"device: {info}")
     assert info["arch"].startswith("gfx950")
+    # dense fp16 peak from CUs and the maximum engine clock (2.5 PFLOP/s class), HBM 8 TB/s
+    expect = info["compute_units"] * info["clock_khz"] * 1e3 * 4096 / 1e12
+    assert abs(info["peak_fp16_tflops"] - expect) < 1e-6 * expect and 1500 < expect < 3500, info
+    assert info["peak_hbm_gbps"] == 8000.0
     inp = ag_inputs(1024, 1024, 256, 4)
     run_ag(inp)
     gs, ge, cs, ce = il.iris_last_windows()
     note(f"windows ns: gemm [{gs:.0f}, {ge:.0f}] comm [{cs:.0f}, {ce:.0f}]")
     assert ge > gs >= 0 and ce > cs >= 0
+    mhz = il.iris_last_clock()
+    note(f"shader clock during the launch: {mhz:.0f} MHz")
+    assert mhz > 0
 
 
 def test_repeat_runs_bit_identical():
@@ -373,7 +382,7 @@ def test_tune_gemm_wgs_and_top_k(tmp_path, monkeypatch):
     """The split sweep benchmarks every candidate (or, with top_k, only the
     best predicted ones, the rest reading -1), returns a benchmarked winner
     that is then used by default, and leaves outputs equal to the oracle's."""
-    monkeypatch.setenv("IRIS_LOCAL_TUNE_CACHE", str(tmp_path / "tune.txt"))
+    monkeypatch.setenv("IRIS_LOCAL_TUNE_CACHE", str(tmp_path / "tune.json"))
     W, M, N, kl = 4, 1024, 1024, 256
     inp = ag_inputs(M, N, kl, W, seed=21)
     shards, B, bias = cuda(inp["shards"]), cuda(inp["B"]), cuda(inp["bias"])
@@ -398,25 +407,41 @@ def test_tune_gemm_wgs_and_top_k(tmp_path, monkeypatch):
         assert_close(C, Cref, f"C after tuning top_k={top_k}")
         C2, G2 = run_ag(inp)  # uses the tuned split from the cache
         assert_bits_equal(C2, C, f"tuned default top_k={top_k}")
+        db = json.load(open(tmp_path / "tune.json"))  # the cache file is one JSON object
+        assert isinstance(db, dict) and best in db.values(), db
+        assert all(k.startswith("gfx950 op1 M1024 N1024 K256 W4") for k in db), db
 
 
 def test_device_wait_bound_reports_timeout(monkeypatch):
     """The host forces a zero poll bound: reduce units that must wait for
-    GEMM tiles give up at once, the launch still ends, and the debug check
-    reports IRIS_ERR_DEVICE_TIMEOUT. With the bound back at its default the
-    same call is correct again (the error word was cleared)."""
+    GEMM tiles give up at once and every launch still ends. Without the debug
+    switch the op returns normally and iris_check_device_error reports the
+    timeout once (then the status is clear); with IRIS_LOCAL_DEBUG the op
+    itself raises. The protocol words are zero again after the failing
+    launches: with the bound back at its default the same call is correct
+    and no error is reported."""
     W, M, N, K = 4, 2048, 2048, 4096
     inp = rs_inputs(M, N, K, W, seed=31)
     ref = oracle.matmul_reduce_scatter(host(inp["A"]), host(inp["B"]), [host(p) for p in inp["partials"]],
                                        W, rank=0, bias=host(inp["bias"]))
     cfg = Config(gemm_wgs=1)  # nearly every workgroup starts on the reduce units and must wait
-    monkeypatch.setenv("IRIS_LOCAL_DEBUG", "1")
+    il.iris_check_device_error()  # nothing pending from earlier tests
     monkeypatch.setenv("IRIS_LOCAL_SPIN_LIMIT", "0")
-    note("mm_rs with a zero poll bound (expect IRIS_ERR_DEVICE_TIMEOUT)")
+    note("mm_rs with a zero poll bound, no debug switch (expect a reported timeout)")
+    run_rs(inp, W, 0, cfg)
+    run_rs(inp, W, 0, cfg)
+    with pytest.raises(il.IrisError) as ei:
+        il.iris_check_device_error()
+    assert ei.value.status == 9, ei.value
+    il.iris_check_device_error()  # read and cleared: reported once
+    monkeypatch.setenv("IRIS_LOCAL_DEBUG", "1")
+    note("mm_rs with a zero poll bound and IRIS_LOCAL_DEBUG (expect IRIS_ERR_DEVICE_TIMEOUT)")
     with pytest.raises(il.IrisError) as ei:
         run_rs(inp, W, 0, cfg)
     assert ei.value.status == 9, ei.value
     monkeypatch.delenv("IRIS_LOCAL_SPIN_LIMIT")
     note("mm_rs with the default poll bound")
-    out, _ = run_rs(inp, W, 0, cfg)
+    out, _ = run_rs(inp, W, 0, cfg)  # debug still on: raises if the status were stale
     assert_close(out, ref, "reduce_scatter after a timed-out call")
+    monkeypatch.delenv("IRIS_LOCAL_DEBUG")
+    il.iris_check_device_error()
