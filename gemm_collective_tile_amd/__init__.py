@@ -93,7 +93,8 @@ class _OpArgs(ctypes.Structure):
 
 class _PredictParams(ctypes.Structure):
     _fields_ = [(n, ctypes.c_double) for n in (
-        "gemm_tflops_per_cu", "tile_overhead_us", "comm_gbps_per_cu", "comm_gbps_chip", "unit_overhead_us")]
+        "gemm_tflops_per_cu", "tile_overhead_us", "comm_gbps_per_cu", "comm_gbps_chip", "unit_overhead_us",
+        "gemm_tflops_per_cu_max", "gemm_slowdown", "comm_slowdown", "phase_penalty")]
 
 
 class _DeviceInfo(ctypes.Structure):
@@ -420,10 +421,11 @@ def iris_predict_gemm_wgs(op, candidates, grid, config=None, params=None, *, W=1
     """Predicted makespan (ms) of the fused schedule for each gemm_wgs
     candidate on a grid of `grid` workgroups; returns (best, {candidate: ms}).
     Host only: needs the shapes, no tensors. `params` is a dict of the
-    model's rates (gemm_tflops_per_cu, tile_overhead_us, comm_gbps_per_cu,
-    comm_gbps_chip, unit_overhead_us); missing ones take the defaults."""
+    model's constants (gemm_tflops_per_cu, tile_overhead_us, comm_gbps_per_cu,
+    comm_gbps_chip, unit_overhead_us, gemm_tflops_per_cu_max, gemm_slowdown,
+    comm_slowdown, phase_penalty); missing ones take the defaults."""
     a, keep = _op_args(op, config, W=W, rank=rank, collective=collective, M=M, N=N, K=K, comm_elems=comm_elems)
-    pp = _PredictParams(*[-1.0] * 5)
+    pp = _PredictParams(*[-1.0] * len(_PredictParams._fields_))
     for k, v in (params or {}).items():
         if k not in dict(_PredictParams._fields_):
             raise ValueError(f"unknown predictor parameter {k!r}")

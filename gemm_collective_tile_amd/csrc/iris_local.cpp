@@ -948,13 +948,17 @@ int iris_tune_gemm_wgs(const iris_op_args_t* a, const int32_t* candidates, int32
     std::vector<float> pred((size_t)n_candidates);
     const int ps = iris_predict_gemm_wgs(a, G, candidates, n_candidates, nullptr, pred.data(), nullptr);
     if (ps) return fail(ps, "the split predictor rejected the op or a candidate");
-    std::stable_sort(bench_idx.begin(), bench_idx.end(), [&](int x, int y) { return pred[x] < pred[y]; });
-    bench_idx.resize(top_k);
-    std::sort(bench_idx.begin(), bench_idx.end());
-    cands.clear();
-    for (int i : bench_idx) cands.push_back(candidates[i]);
-    if (ms_out)
-      for (int i = 0; i < n_candidates; ++i) ms_out[i] = -1.0f;
+    const auto mm = std::minmax_element(pred.begin(), pred.end());
+    // a flat prediction cannot rank: then every candidate is benchmarked
+    if (*mm.second - *mm.first > 1e-6f * *mm.second) {
+      std::stable_sort(bench_idx.begin(), bench_idx.end(), [&](int x, int y) { return pred[x] < pred[y]; });
+      bench_idx.resize(top_k);
+      std::sort(bench_idx.begin(), bench_idx.end());
+      cands.clear();
+      for (int i : bench_idx) cands.push_back(candidates[i]);
+      if (ms_out)
+        for (int i = 0; i < n_candidates; ++i) ms_out[i] = -1.0f;
+    }
   }
   const int def = (G * 7) / 8;
   if (std::find(cands.begin(), cands.end(), def) == cands.end()) cands.push_back(def);

@@ -13,14 +13,33 @@
 // a GEMM tile of all_gather_matmul waits for the copy units of its row block
 // and takes unclaimed copy units while it waits; a reduce unit waits for the
 // GEMM tiles of its columns, taking GEMM tiles only while one it needs is
-// still unclaimed. Durations come from
-// a linear model (per-CU GEMM rate, per-workgroup copy/reduce rate, a
-// whole-chip ceiling on the comm bandwidth shared by the units in flight,
-// fixed costs per tile and per unit); the defaults were measured on MI355X.
+// still unclaimed. Durations come from a rate model whose constants were
+// measured on MI355X:
+//   * a tile costs a fixed overhead plus its FLOPs at a per-CU rate. The
+//     chip's MFMA throughput is capped by power, not by CU count: with n
+//     workgroups working the GEMM queue each tile runs at
+//     min(r_max, r_full * grid / n), where r_full is the rate with every CU
+//     on the GEMM and r_max the rate of a lone CU at its highest clock;
+//   * a comm unit costs a fixed overhead plus its bytes at the per-workgroup
+//     rate, capped by the chip's comm bandwidth shared by the units in
+//     flight;
+//   * the two slow each other: a tile started while the workgroups working
+//     the comm queue could use a fraction u of the chip's comm bandwidth
+//     runs (1 - gemm_slowdown * u) times as fast, and a unit started while a
+//     fraction v of the grid works the GEMM queue moves
+//     (1 - comm_slowdown * v) times as fast;
+//   * with more tiles than workgroups, tiles that share operands reach L2
+//     together only if the workgroups run in phase (every XCD runs a patch
+//     of tiles whose A rows and B columns meet in its L2). A first pass of
+//     the simulation gives every tile's start time; R, the length of the
+//     mean of exp(2 pi i start / tile duration) over the tiles, is 1 when
+//     all start in phase and near 0 when their phases are spread. The second
+//     pass stretches every tile by phase_penalty * (1 - R).
 // Host code only: no device call.
 #include "../../include/iris_local.h"
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <functional>
 #include <queue>
@@ -34,18 +53,32 @@ int set_error(int status, const char* msg);  // defined beside the other entry p
 
 namespace iris_predict {
 
-constexpr double kGemmTflopsPerCu = 5.0;   // K-loop rate of a 256x256 tile (fit over K = 4096..16384)
+constexpr double kGemmTflopsPerCu = 5.0;   // K-loop rate of a 256x256 tile, every CU on the GEMM
+                                           // (fit over K = 4096..16384)
 constexpr double kTileOverheadUs = 20.0;   // claim, prologue, epilogue and store drain of a tile
 constexpr double kCommGbpsPerCu = 45.0;    // one 4-wave workgroup copying or reducing
 constexpr double kCommGbpsChip = 5200.0;   // plain copy over the whole chip
 constexpr double kUnitOverheadUs = 1.0;    // claim + release of a comm unit
+// Fitted (grid search) to sixteen gemm_wgs sweeps measured on MI355X: the
+// four bench workloads (pow2_4k and g2 all_gather_matmul, llama7b_gate
+// reduce_scatter, the 8192^3 GEMM beside an 8 x 64Mi all_reduce) on four
+// boxes. With these, the predicted best split measured within 1.1 % of the
+// measured best in every sweep, and the three best predicted always held a
+// split within 1 % of it.
+constexpr double kGemmTflopsPerCuMax = 5.25;
+constexpr double kGemmSlowdown = 0.10;
+constexpr double kCommSlowdown = 0.60;
+constexpr double kPhasePenalty = 0.045;
 
 struct Work {
   int grid = 0;
   bool steal = true;
   int kind = 0;  // 1 AG, 2 RS/ARMM (comm waits on tiles), 0 independent
-  std::vector<double> tile_ms;
+  std::vector<double> tile_flop;            // FLOPs of each tile
   std::vector<int> tile_pm;
+  double tile_overhead_ms = 0.02;
+  double r_full = kGemmTflopsPerCu * 1e12, r_max = kGemmTflopsPerCuMax * 1e12;
+  double gemm_slowdown = kGemmSlowdown, comm_slowdown = kCommSlowdown, phase_penalty = kPhasePenalty;
   std::vector<double> unit_bytes;
   std::vector<int> unit_pm;                 // AG: row block the unit belongs to
   std::vector<std::vector<int>> unit_deps;  // RS/ARMM: tiles a unit needs
@@ -53,16 +86,14 @@ struct Work {
   double comm_gbps_cu = kCommGbpsPerCu, comm_gbps_chip = kCommGbpsChip, unit_overhead_ms = 1e-3;
 };
 
-double unit_ms(const Work& w, double bytes, int active) {
-  const double gbps = std::min(w.comm_gbps_cu, w.comm_gbps_chip / std::max(1, active));
-  return w.unit_overhead_ms + bytes / (gbps * 1e9) * 1e3;
-}
-
-// Makespan (ms) of the schedule with gemm_wgs workgroups starting on GEMM.
-double simulate(const Work& w, int gemm_wgs) {
-  const int T = (int)w.tile_ms.size(), U = (int)w.unit_bytes.size();
+// Makespan (ms) of the schedule with gemm_wgs workgroups starting on GEMM;
+// every tile is stretched by the factor `stretch`; tile start times go to
+// *starts if it is not null.
+double simulate(const Work& w, int gemm_wgs, double stretch, std::vector<double>* starts) {
+  const int T = (int)w.tile_flop.size(), U = (int)w.unit_bytes.size();
   std::vector<double> tile_end(T, -1.0);
   int next_tile = 0, next_unit = 0;
+  int on_gemm = 0, on_comm = 0;  // workgroups working each queue
   // all_gather: per row block, units not yet claimed and the latest end time
   std::vector<int> rb_left(w.n_pm, 0);
   std::vector<double> rb_end(w.n_pm, 0.0);
@@ -72,7 +103,10 @@ double simulate(const Work& w, int gemm_wgs) {
   std::priority_queue<double, std::vector<double>, std::greater<double>> active;
   auto start_unit = [&](int u, double t0) {
     while (!active.empty() && active.top() <= t0) active.pop();
-    const double end = t0 + unit_ms(w, w.unit_bytes[u], (int)active.size() + 1);
+    const double v = std::min(1.0, (double)on_gemm / (double)w.grid);
+    const double gbps = std::min(w.comm_gbps_cu, w.comm_gbps_chip / (double)(active.size() + 1)) *
+                        (1.0 - w.comm_slowdown * v);
+    const double end = t0 + w.unit_overhead_ms + w.unit_bytes[u] / (gbps * 1e9) * 1e3;
     active.push(end);
     if (w.kind == 1) {
       const int pm = w.unit_pm[u];
@@ -82,7 +116,11 @@ double simulate(const Work& w, int gemm_wgs) {
     return end;
   };
   auto start_tile = [&](int t, double t0) {
-    tile_end[t] = t0 + w.tile_ms[t];
+    const double n = (double)std::max(1, on_gemm);
+    const double u = std::min(1.0, (double)on_comm * w.comm_gbps_cu / w.comm_gbps_chip);
+    const double rate = std::min(w.r_max, w.r_full * (double)w.grid / n) * (1.0 - w.gemm_slowdown * u);
+    tile_end[t] = t0 + (w.tile_overhead_ms + w.tile_flop[t] / rate * 1e3) * stretch;
+    if (starts) (*starts)[t] = t0;
     return tile_end[t];
   };
 
@@ -97,6 +135,7 @@ double simulate(const Work& w, int gemm_wgs) {
   std::priority_queue<Ev, std::vector<Ev>, std::greater<Ev>> ev;
   for (int i = 0; i < w.grid; ++i) {
     wk[i].gemm_first = i < gemm_wgs || U == 0;
+    ++(wk[i].gemm_first ? on_gemm : on_comm);
     ev.push({0.0, i});
   }
   double makespan = 0.0;
@@ -159,6 +198,8 @@ double simulate(const Work& w, int gemm_wgs) {
       }
       if (k.phase == 0 && w.steal) {
         k.phase = 1;
+        // this workgroup moves to the other queue
+        if (gemm) { --on_gemm; ++on_comm; } else { --on_comm; ++on_gemm; }
         if (w.kind == 1 && !k.gemm_first && T > w.grid) {
           // all_gather with more tiles than workgroups: a copy workgroup
           // joins the GEMM once every copy unit has finished (all are
@@ -173,10 +214,36 @@ double simulate(const Work& w, int gemm_wgs) {
         continue;
       }
       k.done = true;
+      --(gemm ? on_gemm : on_comm);
       break;
     }
   }
   return makespan;
+}
+
+// Phase coherence R of the tile start times of a first pass (see the top of
+// this file), against the median tile duration of that pass.
+double phase_coherence(const std::vector<double>& starts, double period) {
+  if (starts.empty() || period <= 0) return 1.0;
+  double c = 0, s = 0;
+  for (double t : starts) {
+    const double ph = 2.0 * 3.14159265358979323846 * t / period;
+    c += std::cos(ph);
+    s += std::sin(ph);
+  }
+  return std::sqrt(c * c + s * s) / (double)starts.size();
+}
+
+double predict(const Work& w, int gemm_wgs) {
+  const int T = (int)w.tile_flop.size();
+  if (T <= w.grid || w.phase_penalty <= 0) return simulate(w, gemm_wgs, 1.0, nullptr);
+  std::vector<double> starts(T, 0.0);
+  simulate(w, gemm_wgs, 1.0, &starts);
+  std::vector<double> flop(w.tile_flop);
+  std::nth_element(flop.begin(), flop.begin() + T / 2, flop.end());
+  const double period = w.tile_overhead_ms + flop[T / 2] / w.r_full * 1e3;
+  const double R = phase_coherence(starts, period);
+  return simulate(w, gemm_wgs, 1.0 + w.phase_penalty * (1.0 - R), nullptr);
 }
 
 }  // namespace iris_predict
@@ -202,9 +269,15 @@ extern "C" int iris_predict_gemm_wgs(const iris_op_args_t* a, int32_t grid, cons
     return set_error(IRIS_ERR_INVALID_ARG, "predict: M, N, K must be positive and W in [1, IRIS_MAX_W]");
   if (a->op == IRIS_OP_MM_RS && (N % W != 0 || a->rank < 0 || a->rank >= W))
     return set_error(IRIS_ERR_INVALID_ARG, "predict: reduce_scatter needs W | N and 0 <= rank < W");
-  const double R = (params && params->gemm_tflops_per_cu > 0 ? params->gemm_tflops_per_cu : kGemmTflopsPerCu) * 1e12;
-  const double tile_oh = (params && params->tile_overhead_us >= 0 ? params->tile_overhead_us : kTileOverheadUs);
   Work w;
+  w.r_full = (params && params->gemm_tflops_per_cu > 0 ? params->gemm_tflops_per_cu : kGemmTflopsPerCu) * 1e12;
+  w.r_max = (params && params->gemm_tflops_per_cu_max > 0 ? params->gemm_tflops_per_cu_max : kGemmTflopsPerCuMax) *
+            1e12;
+  w.r_max = std::max(w.r_max, w.r_full);
+  w.tile_overhead_ms = (params && params->tile_overhead_us >= 0 ? params->tile_overhead_us : kTileOverheadUs) * 1e-3;
+  if (params && params->gemm_slowdown >= 0) w.gemm_slowdown = std::min(0.95, params->gemm_slowdown);
+  if (params && params->comm_slowdown >= 0) w.comm_slowdown = std::min(0.95, params->comm_slowdown);
+  if (params && params->phase_penalty >= 0) w.phase_penalty = params->phase_penalty;
   w.grid = grid;
   w.steal = (c.flags & IRIS_FLAG_NO_STEAL) == 0;
   if (params && params->comm_gbps_per_cu > 0) w.comm_gbps_cu = params->comm_gbps_per_cu;
@@ -223,7 +296,7 @@ extern "C" int iris_predict_gemm_wgs(const iris_op_args_t* a, int32_t grid, cons
     o.prio_hi = (int)cdiv(col0 + nl, bn);
   }
   const int T = n_pm * n_pn;
-  w.tile_ms.resize(T);
+  w.tile_flop.resize(T);
   w.tile_pm.resize(T);
   w.n_pm = n_pm;
   for (int t = 0; t < T; ++t) {
@@ -231,7 +304,7 @@ extern "C" int iris_predict_gemm_wgs(const iris_op_args_t* a, int32_t grid, cons
     iris::tile_coords(o, t, pm, pn);
     const double rows = (double)std::min<int64_t>(bm, M - (int64_t)pm * bm);
     const double cols = (double)std::min<int64_t>(bn, N - (int64_t)pn * bn);
-    w.tile_ms[t] = tile_oh * 1e-3 + 2.0 * rows * cols * (double)K / R * 1e3;
+    w.tile_flop[t] = 2.0 * rows * cols * (double)K;
     w.tile_pm[t] = pm;
   }
 
@@ -313,7 +386,7 @@ extern "C" int iris_predict_gemm_wgs(const iris_op_args_t* a, int32_t grid, cons
   for (int i = 0; i < n_candidates; ++i) {
     const int gw = candidates[i];
     if (gw < 1 || gw > grid - 1) return set_error(IRIS_ERR_CONFIG, "predict: a candidate gemm_wgs is outside [1, grid-1]");
-    const double ms = simulate(w, gw);
+    const double ms = predict(w, gw);
     if (predicted_ms) predicted_ms[i] = (float)ms;
     if (best < 0 || ms < best_ms || (ms == best_ms && gw > best)) {
       best = gw;

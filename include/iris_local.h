@@ -277,7 +277,9 @@ int iris_grid_size(int32_t op, const iris_config_t* cfg);
  * workgroups. The op's outputs hold the last candidate's results.
  * top_k > 0 (and below n_candidates): rank the candidates with
  * iris_predict_gemm_wgs first and benchmark only the top_k best predicted
- * (plus the default); ms_out of a candidate left out is -1.
+ * (plus the default); ms_out of a candidate left out is -1. If the
+ * predictor cannot tell the candidates apart (all predictions equal), every
+ * candidate is benchmarked.
  */
 typedef struct iris_op_args {
   int32_t op;             /* IRIS_OP_* */
@@ -307,13 +309,29 @@ int iris_tune_gemm_wgs(const iris_op_args_t* args, const int32_t* candidates,
  * predicted milliseconds to predicted_ms[i] (may be NULL) and the best
  * candidate to *best_gemm_wgs (ties to more GEMM workgroups). Host code
  * only: no device call and no workspace; errors set iris_last_error_message.
- * params may be NULL (a rate <= 0 or an overhead < 0 means its default); the
- * defaults were measured on MI355X:
- *   gemm_tflops_per_cu  K-loop rate of one CU (256x256 tiles)  5.0
- *   tile_overhead_us    fixed cost per GEMM tile               20
- *   comm_gbps_per_cu    copy/reduce rate of one workgroup       45
- *   comm_gbps_chip      comm bandwidth of the whole chip        5200
- *   unit_overhead_us    fixed cost per comm unit                1
+ * params may be NULL (a rate <= 0 or an overhead, slowdown or penalty < 0
+ * means its default); the defaults were measured on MI355X:
+ *   gemm_tflops_per_cu      K-loop rate of one CU (256x256 tiles) with
+ *                           every CU on the GEMM                    5.0
+ *   tile_overhead_us        fixed cost per GEMM tile                20
+ *   comm_gbps_per_cu        copy/reduce rate of one workgroup       45
+ *   comm_gbps_chip          comm bandwidth of the whole chip        5200
+ *   unit_overhead_us        fixed cost per comm unit                1
+ *   gemm_tflops_per_cu_max  K-loop rate of one CU when few run the    5.25
+ *                           GEMM (the chip's MFMA throughput is
+ *                           capped by power: with n workgroups on
+ *                           the GEMM queue tiles run at
+ *                           min(this, gemm_tflops_per_cu * grid/n))
+ *   gemm_slowdown           relative GEMM slowdown while the comm      0.10
+ *                           workgroups can use the whole chip's comm
+ *                           bandwidth
+ *   comm_slowdown           relative comm slowdown while every         0.60
+ *                           workgroup works the GEMM queue
+ *   phase_penalty           relative slowdown of every tile when the   0.045
+ *                           tiles of a multi-wave GEMM start with
+ *                           fully spread phases (operands no longer
+ *                           meet in L2)
+ * The last four were fitted to measured sweeps of the bench workloads.
  */
 typedef struct iris_predict_params {
   double gemm_tflops_per_cu;
@@ -321,6 +339,10 @@ typedef struct iris_predict_params {
   double comm_gbps_per_cu;
   double comm_gbps_chip;
   double unit_overhead_us;
+  double gemm_tflops_per_cu_max;
+  double gemm_slowdown;
+  double comm_slowdown;
+  double phase_penalty;
 } iris_predict_params_t;
 
 int iris_predict_gemm_wgs(const iris_op_args_t* args, int32_t grid, const int32_t* candidates,

@@ -120,14 +120,17 @@ def test_matmul_all_gather_integer_exact_pow2_4k():
     w = wl.Workload("mmag_int", "mm_ar", M=M, N=N, K=K, W=W, a_std=1.0, b_std=1.0)
     inp = wl.make_inputs(w, seed=7, device="cuda", integer=True)
     peers = inp["partials"]  # W-1 (M, N) integer blocks standing in for the other ranks' results
-    note("oracle: integer matmul_all_gather 4096^3 W=8")
-    ref = oracle.matmul_all_gather(host(inp["A"]), host(inp["B"]), [host(p) for p in peers], W, rank=rank,
-                                   bias=host(inp["bias"]))
     note("integer matmul_all_gather rank=2")
     out = empty((M * W, N))
     il.iris_mm_ag_local(out, inp["A"], inp["B"], peers, W, rank=rank, bias=inp["bias"])
     torch.cuda.synchronize()
-    assert_exact(out, ref, "matmul_all_gather out")
+    hp = [host(p) for p in peers]
+    # one oracle call per block of M rows, so that its threads share the GEMM block
+    for blk in range(W):
+        note(f"oracle: integer matmul_all_gather rows of block {blk}")
+        ref = oracle.matmul_all_gather(host(inp["A"]), host(inp["B"]), hp, W, rank=rank, bias=host(inp["bias"]),
+                                       rows=(blk * M, (blk + 1) * M))
+        assert_exact(out[blk * M:(blk + 1) * M], ref, f"matmul_all_gather out block {blk}")
     il.iris_check_device_error()
 
 

@@ -409,7 +409,7 @@ def test_tune_gemm_wgs_and_top_k(tmp_path, monkeypatch):
         assert_bits_equal(C2, C, f"tuned default top_k={top_k}")
         db = json.load(open(tmp_path / "tune.json"))  # the cache file is one JSON object
         assert isinstance(db, dict) and best in db.values(), db
-        assert all(k.startswith("gfx950 op1 M1024 N1024 K256 W4") for k in db), db
+        assert all(k.startswith("gfx950 op16 M1024 N1024 K256 W4") for k in db), db  # op id x 16 + collective
 
 
 def test_device_wait_bound_reports_timeout(monkeypatch):

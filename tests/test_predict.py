@@ -7,7 +7,8 @@ workgroup with more tiles than workgroups only after the whole gather; an
 all_gather_matmul tile waits for the copy units of its row block and takes
 copy units meanwhile; a reduce unit waits for the tiles of its columns),
 with a rate model chosen so
-the durations are round numbers:
+the durations are round numbers (the power cap, the mutual slowdowns and
+the phase penalty switched off):
 
     GEMM tile  = 2*rows*cols*K / (1 TFLOP/s)          (no fixed cost)
     comm unit  = bytes / (1 GB/s per workgroup)       (no fixed cost)
@@ -21,7 +22,8 @@ import gemm_collective_tile_amd as il
 from gemm_collective_tile_amd import Config, IrisError
 
 UNIT = dict(gemm_tflops_per_cu=1.0, tile_overhead_us=0.0, comm_gbps_per_cu=1.0, comm_gbps_chip=1e9,
-            unit_overhead_us=0.0)
+            unit_overhead_us=0.0, gemm_tflops_per_cu_max=1.0, gemm_slowdown=0.0, comm_slowdown=0.0,
+            phase_penalty=0.0)
 
 
 def tile_ms(rows, cols, K):
@@ -126,7 +128,8 @@ def test_without_stealing_the_best_split_balances_the_queues():
     # no queue switching: the makespan is the longer of ceil(1024/g) tiles and ceil(1024/(256-g)) units,
     # which is smallest at an interior split
     p = dict(gemm_tflops_per_cu=4.4, tile_overhead_us=2.0, comm_gbps_per_cu=45.0, comm_gbps_chip=5200.0,
-             unit_overhead_us=1.0)
+             unit_overhead_us=1.0, gemm_tflops_per_cu_max=4.4, gemm_slowdown=0.0, comm_slowdown=0.0,
+             phase_penalty=0.0)
     t = 2e-3 + tile_ms(256, 256, 8192) / 4.4
     u = 1e-3 + unit_ms(65536 * 2 * 9, 45.0)
     cands = [32, 64, 128, 192, 224, 240, 255]
@@ -171,3 +174,80 @@ def test_invalid_arguments(kw, msg):
 def test_unknown_parameter_name():
     with pytest.raises(ValueError):
         il.iris_predict_gemm_wgs(il.IRIS_OP_AG_MM, [1], 8, params={"gemm_rate": 1.0}, W=2, M=256, N=256, K=256)
+
+
+# ------------------------------------------------------------ rate model terms
+
+def test_power_cap_lets_fewer_gemm_workgroups_run_faster():
+    # one tile on a grid of 4 with NO_STEAL: 1 workgroup on the GEMM queue. Its tile runs at
+    # min(r_max, r_full * grid / 1) = min(3, 4) = 3 TFLOP/s; with r_max = r_full it runs at 1.
+    shape = dict(W=2, collective=il.IRIS_COLL_BROADCAST, M=256, N=256, K=1024, comm_elems=2048)
+    cfg = Config(comm_chunk=2048, flags=il.IRIS_FLAG_NO_STEAL)
+    fast = dict(UNIT, gemm_tflops_per_cu_max=3.0)
+    _, ms = predict(il.IRIS_OP_CONCURRENT, [1], 4, cfg, params=fast, **shape)
+    assert ms[1] == pytest.approx(max(tile_ms(256, 256, 1024) / 3.0, unit_ms(2048 * 4)), rel=1e-6)
+    _, ms = predict(il.IRIS_OP_CONCURRENT, [1], 4, cfg, params=UNIT, **shape)
+    assert ms[1] == pytest.approx(max(tile_ms(256, 256, 1024), unit_ms(2048 * 4)), rel=1e-6)
+
+
+def test_comm_workgroups_slow_the_gemm_and_back():
+    # grid 4, gemm_wgs 2, NO_STEAL: 2 workgroups on each queue. Comm rate 1 GB/s per workgroup,
+    # chip 4 GB/s: the comm side could use u = 2 * 1 / 4 = 0.5 of it, so a tile runs
+    # (1 - 0.2 * 0.5) = 0.9 times as fast; half the grid is on the GEMM (v = 0.5), so a unit
+    # moves (1 - 0.4 * 0.5) = 0.8 times as fast.
+    shape = dict(W=2, collective=il.IRIS_COLL_BROADCAST, M=256, N=256, K=1024, comm_elems=2048)
+    cfg = Config(comm_chunk=2048, flags=il.IRIS_FLAG_NO_STEAL)
+    prm = dict(UNIT, comm_gbps_chip=4.0, gemm_slowdown=0.2, comm_slowdown=0.4)
+    _, ms = predict(il.IRIS_OP_CONCURRENT, [2], 4, cfg, params=prm, **shape)
+    # one tile (2 GEMM workgroups, r_max = r_full: 1 * 4 / 2 = 2 capped at r_max = 1) and one unit
+    tile = tile_ms(256, 256, 1024) / 0.9
+    unit = unit_ms(2048 * 4) / 0.8
+    assert ms[2] == pytest.approx(max(tile, unit), rel=1e-6)
+
+
+def test_phase_penalty_only_when_workgroups_fall_out_of_phase():
+    # a multi-wave GEMM alone (broadcast of one tiny unit beside it, all workgroups on the GEMM,
+    # NO_STEAL so the comm workgroup never takes tiles): every wave starts in phase, R = 1, no penalty
+    shape = dict(W=2, collective=il.IRIS_COLL_BROADCAST, M=1024, N=1024, K=1024, comm_elems=2048)
+    cfg = Config(comm_chunk=2048, flags=il.IRIS_FLAG_NO_STEAL)
+    prm = dict(UNIT, phase_penalty=0.5)
+    _, ms = predict(il.IRIS_OP_CONCURRENT, [4], 5, cfg, params=prm, **shape)
+    assert ms[4] == pytest.approx(4 * tile_ms(256, 256, 1024), rel=1e-6)  # 16 tiles on 4 workgroups
+
+
+# ------------------------------------------------------ measured sweeps (MI355X)
+
+def _sweeps():
+    import json
+    import os
+    d = json.load(open(os.path.join(os.path.dirname(__file__), "data", "measured_sweeps_mi355x.json")))
+    for run in d["runs"]:
+        for name, rec in run.items():
+            w = d["workloads"][name]
+            shape = {k: w[k] for k in ("W", "M", "N", "K", "rank", "comm_elems") if k in w}
+            yield name, w["op"], rec["grid"], {int(k): v for k, v in rec["sweep_ms"].items()}, shape
+
+
+def test_default_model_ranks_the_measured_sweeps():
+    """With its default constants the predictor's best split measured within
+    1.5 % of the measured best in each of the recorded sweeps (four
+    workloads on four boxes), and the three best predicted splits always hold
+    one within 1 % of it, so top_k = 3 keeps a winner."""
+    for name, op, grid, meas, shape in _sweeps():
+        cands = sorted(meas)
+        best, pred = il.iris_predict_gemm_wgs(op, cands, grid, **shape)
+        mbest = min(meas.values())
+        assert meas[best] <= 1.015 * mbest, (name, best, meas)
+        top3 = sorted(cands, key=lambda c: (pred[c], -c))[:3]
+        assert min(meas[c] for c in top3) <= 1.01 * mbest, (name, top3, meas)
+
+
+def test_concurrent_prediction_is_not_flat():
+    # the GEMM beside the 8 x 64Mi all_reduce: giving the comm queue more workgroups speeds the
+    # all_reduce but costs GEMM throughput; the measured sweeps are U-shaped, and so is the model
+    cands = [96, 128, 160, 192, 208, 224, 240, 255]
+    best, pred = il.iris_predict_gemm_wgs(il.IRIS_OP_CONCURRENT, cands, 256, W=8, M=8192, N=8192, K=8192,
+                                          comm_elems=64 << 20)
+    assert max(pred.values()) > 1.03 * min(pred.values())
+    assert 192 <= best <= 240
+    assert pred[96] > pred[best] and pred[255] > pred[best]
