@@ -115,6 +115,7 @@ def _load() -> ctypes.CDLL:
     cfgp = ctypes.POINTER(_Config)
     sig = {
         "iris_ag_mm": [vp, vp, vpp, i32, vp, vp, i64, i64, i64, cfgp, vp, sz, vp],
+        "iris_ag_mm_noalloc": [vp, vp, vpp, i32, vp, vp, i64, i64, i64, cfgp, vp],
         "iris_mm_rs_local": [vp, vp, vp, vp, vp, vpp, i32, i32, i64, i64, i64, cfgp, vp, sz, vp],
         "iris_mm_ar_local": [vp, vp, vp, vp, vp, vpp, i32, i64, i64, i64, cfgp, vp, sz, vp],
         "iris_concurrent": [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vpp, i32, i64, cfgp, vp, sz, vp],
@@ -311,6 +312,21 @@ def iris_ag_mm(C, A_gathered, A_shards, B, bias=None, config=None, workspace=Non
     _check(_lib.iris_ag_mm(_ptr(C, "C"), _ptr(A_gathered, "A_gathered"), _ptr_array(A_shards, "A_shards"),
                            W, _ptr(B, "B"), _ptr(bias, "bias", True), M, N, K_local, _cfg(config),
                            ws, wsb, _stream(stream)))
+
+
+def iris_ag_mm_noalloc(C, A_gathered, A_shards, B, bias=None, config=None, stream=None):
+    """iris_ag_mm on the library's static device scratch (no workspace, no
+    allocation); calls that overlap in time on one GPU race."""
+    W = len(A_shards)
+    if W < 1:
+        raise ValueError("A_shards is empty")
+    M, K_local = _shape2(A_shards[0], "A_shards[0]")
+    N = _shape2(B, "B")[1]
+    _validate(IRIS_OP_AG_MM, config, C=C, out=A_gathered, srcs=A_shards, W=W, B=B, bias=bias, M=M, N=N,
+              K=K_local)
+    _check(_lib.iris_ag_mm_noalloc(_ptr(C, "C"), _ptr(A_gathered, "A_gathered"),
+                                   _ptr_array(A_shards, "A_shards"), W, _ptr(B, "B"), _ptr(bias, "bias", True),
+                                   M, N, K_local, _cfg(config), _stream(stream)))
 
 
 def iris_mm_rs_local(out, C, A, B, partials, W, rank=0, bias=None, config=None, workspace=None,

@@ -711,12 +711,10 @@ int set_error(int status, const char* msg) {
 }
 }  // namespace iris
 
-extern "C" {
-
-int iris_ag_mm(void* C, void* A_gathered, const void* const* A_shards, int32_t W, const void* B,
-               const void* bias, int64_t M, int64_t N, int64_t K_local, const iris_config_t* cfg,
-               void* workspace, size_t workspace_bytes, void* stream) {
-  g_msg.clear();
+namespace {
+// Arguments of iris_ag_mm and iris_ag_mm_noalloc, checked before any HIP call.
+int check_ag_mm(void* C, void* A_gathered, const void* const* A_shards, int32_t W, const void* B,
+                const void* bias, int64_t M, int64_t N, int64_t K_local) {
   if (W < 1 || W > IRIS_MAX_W) return fail(IRIS_ERR_INVALID_ARG, "W must be in [1, %d] (got %d)", IRIS_MAX_W, W);
   int st;
   if ((st = check_ptr(C, "C")) || (st = check_ptr(A_gathered, "A_gathered")) || (st = check_ptr(B, "B")) ||
@@ -724,7 +722,18 @@ int iris_ag_mm(void* C, void* A_gathered, const void* const* A_shards, int32_t W
     return st;
   if (K_local <= 0) return fail(IRIS_ERR_INVALID_ARG, "K_local must be positive");
   if (K_local % 8 != 0) return fail(IRIS_ERR_ALIGNMENT, "K_local must be a multiple of 8 (got %lld)", (long long)K_local);
-  if ((st = check_gemm_dims(M, N, K_local * W))) return st;
+  return check_gemm_dims(M, N, K_local * W);
+}
+}  // namespace
+
+extern "C" {
+
+int iris_ag_mm(void* C, void* A_gathered, const void* const* A_shards, int32_t W, const void* B,
+               const void* bias, int64_t M, int64_t N, int64_t K_local, const iris_config_t* cfg,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  g_msg.clear();
+  int st = check_ag_mm(C, A_gathered, A_shards, W, B, bias, M, N, K_local);
+  if (st) return st;
   OpDesc d{};
   d.kind = iris::OP_AG;
   d.iris_op = IRIS_OP_AG_MM;
@@ -739,6 +748,30 @@ int iris_ag_mm(void* C, void* A_gathered, const void* const* A_shards, int32_t W
   d.K = K_local * W;
   d.K_local = K_local;
   return run(d, cfg, workspace, workspace_bytes, stream);
+}
+
+int iris_ag_mm_noalloc(void* C, void* A_gathered, const void* const* A_shards, int32_t W, const void* B,
+                       const void* bias, int64_t M, int64_t N, int64_t K_local, const iris_config_t* cfg,
+                       void* stream) {
+  g_msg.clear();
+  int st = check_ag_mm(C, A_gathered, A_shards, W, B, bias, M, N, K_local);
+  if (st) return st;
+  Resolved r{};
+  if ((st = resolve_static(cfg, &r))) return st;
+  // the workspace this op needs is known from the shape and tile alone
+  const size_t need = int_region_bytes(flag_words(iris::OP_AG, M, N, W, r.bm, r.bn)) + kStampBytes;
+  if (need > iris::kScratchBytes)
+    return fail(IRIS_ERR_WORKSPACE,
+                "iris_ag_mm_noalloc needs %zu bytes of workspace for M=%lld with %dx%d tiles; its static scratch "
+                "holds %zu (use iris_ag_mm with a workspace)",
+                need, (long long)M, r.bm, r.bn, iris::kScratchBytes);
+  int dev = 0;
+  DevInfo di;
+  if ((st = current_device(&dev, &di))) return st;
+  void* ws = nullptr;
+  const hipError_t e = iris::scratch_setup(dev, (hipStream_t)stream, &ws);
+  if (e != hipSuccess) return hip_fail(e, "static scratch set-up");
+  return iris_ag_mm(C, A_gathered, A_shards, W, B, bias, M, N, K_local, cfg, ws, iris::kScratchBytes, stream);
 }
 
 int iris_mm_rs_local(void* out, void* C, const void* A, const void* B, const void* bias,
@@ -1131,19 +1164,28 @@ int iris_last_clock(void* workspace, void* stream, double* mhz) {
 
 int iris_check_device_error(void* workspace, void* stream) {
   g_msg.clear();
-  void* ws = workspace;
-  if (!ws) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (workspace) {
+    if ((uintptr_t)workspace % 256 != 0) return fail(IRIS_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+    return read_status(workspace, (hipStream_t)stream);
+  }
+  // the library's own workspace for this stream and the device's static
+  // scratch (iris_ag_mm_noalloc), each if it has been used
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  void* own = nullptr;
+  {
     std::lock_guard<std::mutex> lk(g_mu);
     auto it = g_ws.find({dev, stream});
-    if (it == g_ws.end() || !it->second.ptr) return IRIS_OK;  // no op has used it: nothing to report
-    ws = it->second.ptr;
-  } else if ((uintptr_t)ws % 256 != 0) {
-    return fail(IRIS_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+    if (it != g_ws.end()) own = it->second.ptr;
   }
-  return read_status(ws, (hipStream_t)stream);
+  int status = IRIS_OK;
+  for (void* ws : {own, iris::scratch_if_set_up(dev)}) {
+    if (!ws) continue;
+    const int st = read_status(ws, (hipStream_t)stream);
+    if (st != IRIS_OK) status = st;
+  }
+  return status;
 }
 
 int iris_device_info(int32_t device, iris_device_info_t* info) {

@@ -29,6 +29,8 @@
 // reduce back by a whole tile.
 #include "launch.hpp"
 
+#include <mutex>
+
 namespace iris {
 
 // ------------------------------------------------------------------ queues
@@ -546,6 +548,55 @@ static int occ_op(int op) {
     case OP_CONC_COPY: return occ_tile<OP_CONC_COPY, BM, BN>();
   }
   return -1;
+}
+
+// ------------------------------------------------------ static scratch
+// The workspace of iris_ag_mm_noalloc, for callers that cannot allocate
+// device memory (code under graph capture, allocation-free serving loops).
+// Each GPU the library runs on holds its own copy until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory:
+// host code uses only the per-device address that hipGetSymbolAddress
+// returns (scratch_setup), never the array's name.
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+__global__ __launch_bounds__(kThreads) void zero_words(uint32_t* p, uint32_t n) {
+  for (uint32_t i = blockIdx.x * kThreads + threadIdx.x; i < n; i += gridDim.x * kThreads) p[i] = 0;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // device address of `scratch` on each device, once set up
+}  // namespace
+
+// Address of this device's scratch. On the first call for a device (which
+// must be current), looks the address up and enqueues a fill kernel that
+// zeroes the array on `s`, ahead of whatever the caller enqueues next (a
+// kernel, not a memset node, so that a caller capturing the first call
+// records a node that replays correctly).
+hipError_t scratch_setup(int dev, hipStream_t s, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    hipLaunchKernelGGL(zero_words, dim3(256), dim3(kThreads), 0, s, (uint32_t*)ptr,
+                       (uint32_t)(kScratchBytes / 4));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
+// The scratch address of `dev` if it has been set up, else null.
+void* scratch_if_set_up(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  return g_scratch[dev];
 }
 
 int persistent_blocks_per_cu(int bm, int bn, int op) {

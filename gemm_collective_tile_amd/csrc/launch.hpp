@@ -67,6 +67,11 @@ struct Params {
   int32_t n_reset;           // words [0, n_reset) (except kStatus) to zero at the end
 };
 
+// Bytes of the static device scratch behind iris_ag_mm_noalloc.
+constexpr size_t kScratchBytes = (size_t)1 << 20;
+hipError_t scratch_setup(int dev, hipStream_t s, void** out);
+void* scratch_if_set_up(int dev);
+
 hipError_t launch_persistent(const Params& p, int bm, int bn, int grid, hipStream_t s);
 hipError_t launch_comm_only(const Params& p, int grid, hipStream_t s);
 // workgroups of the persistent kernel resident per CU, or <= 0 on error

@@ -182,6 +182,25 @@ int iris_ag_mm(void* C, void* A_gathered, const void* const* A_shards, int32_t W
                size_t workspace_bytes, void* stream);
 
 /*
+ * iris_ag_mm without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, allocation-free serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, results and modes as
+ * iris_ag_mm; the workspace is a static device array of 1 MiB that each GPU
+ * the library runs on holds until the process ends, so this entry point
+ * calls no allocator. Sizes whose workspace (iris_workspace_size) exceeds
+ * 1 MiB give IRIS_ERR_WORKSPACE before any HIP call (at 256x256 tiles:
+ * M up to about 1.7 million rows). The first call on a device enqueues a
+ * kernel that zeroes the array on `stream` ahead of the op. Every call on a
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must not be made; calls in stream order
+ * are fine, since each op leaves the array zeroed for the next.
+ * iris_check_device_error(NULL, stream) also reports the array's status.
+ */
+int iris_ag_mm_noalloc(void* C, void* A_gathered, const void* const* A_shards, int32_t W,
+                       const void* B, const void* bias, int64_t M, int64_t N,
+                       int64_t K_local, const iris_config_t* cfg, void* stream);
+
+/*
  * matmul_reduce_scatter, local share for rank `rank` of W
  * ([DOCS] matmul_reduce_scatter, along N):
  *   C = A @ B + bias                                         (M, N)
@@ -373,7 +392,8 @@ int iris_last_clock(void* workspace, void* stream, double* mhz);
 
 /*
  * Device-side errors since the last check on `workspace` (NULL: the
- * library's own workspace for `stream`). Waits for `stream`, then returns
+ * library's own workspace for `stream` and the device's static scratch of
+ * iris_ag_mm_noalloc). Waits for `stream`, then returns
  * IRIS_ERR_DEVICE_TIMEOUT (and clears the status) if a device-side wait of
  * any fused op on that workspace gave up since the last check: the outputs
  * of those ops are then not to be trusted. IRIS_OK otherwise, also when no
