@@ -252,17 +252,21 @@ extern "C" void oracle_matmul_all_gather(
     int64_t K, int64_t m0, int64_t m1, double* out, int nthreads) {
   /* output row r belongs to the block of rank r / M; this rank's block is
    * its own A @ B + bias, every other block is that rank's stand-in result,
-   * peers being listed in rank order without this rank */
-  for (int64_t r = m0; r < m1; ++r) {
-    const int64_t q = r / M, row = r - q * M;
-    double* o = out + (r - m0) * N;
+   * peers being listed in rank order without this rank. The requested rows
+   * are taken block by block, so that the rows of this rank's block go to
+   * the GEMM in one call (which shares them among its threads). */
+  for (int64_t r0 = m0; r0 < m1;) {
+    const int64_t q = r0 / M, row = r0 - q * M;
+    const int64_t r1 = std::min(m1, (q + 1) * M); /* end of block q in range */
+    double* o = out + (r0 - m0) * N;
     if (q == rank) {
-      oracle_gemm_bias(A, K, B, N, bias, bias_mode, K, row, row + 1, 0, N, o,
-                       nthreads);
+      oracle_gemm_bias(A, K, B, N, bias, bias_mode, K, row, row + (r1 - r0), 0,
+                       N, o, nthreads);
     } else {
       const uint16_t* src = peers[q < rank ? q : q - 1] + row * N;
-      for (int64_t n = 0; n < N; ++n) o[n] = oracle_f16_decode(src[n]);
+      for (int64_t i = 0; i < (r1 - r0) * N; ++i) o[i] = oracle_f16_decode(src[i]);
     }
+    r0 = r1;
   }
   (void)W;
 }
