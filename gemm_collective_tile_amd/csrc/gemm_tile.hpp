@@ -129,8 +129,7 @@ struct GemmPipe {
   uint32_t ra_base[S::NSL];   // A, per k slice
   uint32_t rb_base[S::FN];    // B, per 32-column block (includes B_RING)
 
-  __device__ __forceinline__ void setup(const GemmArgs& g, int n0) {
-    const uint32_t tid = threadIdx.x;
+  __device__ __forceinline__ void setup(const GemmArgs& g, int n0, uint32_t tid) {
     const uint32_t l = tid & 63;
     const uint32_t w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t wm = w >> 1, wn = w & 1;
@@ -434,8 +433,16 @@ template <class S>
 __device__ void gemm_tile(const GemmArgs& g, int m0, int n0, char* lds) {
   using P_t = GemmPipe<S>;
   constexpr int NR = S::FM + S::FN;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // The thread id is made opaque here, once per tile, so that every offset
+  // derived from it is recomputed per tile (a few VALU operations) instead
+  // of being hoisted out of the persistent tile loop, kept live across the
+  // K loop and spilled: the spilled offsets came back as about fourteen
+  // serial scratch reloads in front of every K loop, each missing in L2
+  // after a tile's worth of operand traffic.
+  uint32_t tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int nk = (g.K + S::BK - 1) / S::BK;
 
@@ -448,20 +455,20 @@ __device__ void gemm_tile(const GemmArgs& g, int m0, int n0, char* lds) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   P_t P;
-  P.setup(g, n0);
+  P.setup(g, n0, tid);
   typename P_t::Frags f0, f1;
   typename P_t::Regs R0, R1;
 
   const int bias_n = g.bias_along_m ? S::BM : S::BN;
   f16 bias_v = (f16)0.0f;
-  if (g.bias && (int)threadIdx.x < bias_n) {
-    const int idx = (g.bias_along_m ? m0 : n0) + (int)threadIdx.x;
+  if (g.bias && (int)tid < bias_n) {
+    const int idx = (g.bias_along_m ? m0 : n0) + (int)tid;
     if (idx < (g.bias_along_m ? g.M : g.N)) bias_v = g.bias[idx];
   }
   load_all<S, 0>(P, P.rsrc(g, m0, n0, 0), R0);
   load_all<S, 0>(P, P.rsrc(g, m0, n0, 1), R1);
   __syncthreads();  // previous users of the LDS are done
-  if (g.bias && (int)threadIdx.x < bias_n) ((f16*)(lds + S::BIAS_OFF))[threadIdx.x] = bias_v;
+  if (g.bias && (int)tid < bias_n) ((f16*)(lds + S::BIAS_OFF))[tid] = bias_v;
   store_all<S, 0>(P, lds, 0, R0);
   __syncthreads();
   read_all<S, 0, NR>(P, lds, 0, f0);

@@ -631,6 +631,10 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
     // 0.5-1.5 % faster on MI355X); the dependent ops run the GEMM on every
     // workgroup and keep blocks of grid / 8
     if (d.kind == iris::OP_CONC_AR || d.kind == iris::OP_CONC_COPY) p.xcd_q = std::max(1, r.gemm_wgs / iris::kXcds);
+    // lockstep rounds only where an XCD queue is dealt in blocks of the
+    // workgroups that work it: beside an independent collective more
+    // workgroups join the GEMM than the blocks were sized for
+    p.lockstep = p.xcd_q * iris::kXcds == r.grid;
     e = iris::launch_persistent(p, r.bm, r.bn, r.grid, s);
     if (e != hipSuccess) return hip_fail(e, "fused launch");
   } else if (r.mode == IRIS_MODE_TWO_STREAM) {
@@ -647,6 +651,7 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
     pg.T_comm = 0;
     pg.gemm_wgs = r.gemm_wgs;
     pg.xcd_q = std::max(1, r.gemm_wgs / iris::kXcds);
+    pg.lockstep = pg.xcd_q * iris::kXcds == r.gemm_wgs;
     Params pc = p;
     pc.op = d.kind;
     pc.fused = 0;
@@ -667,6 +672,7 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
     pg.fused = 0;
     pg.T_comm = 0;
     pg.gemm_wgs = r.grid;
+    pg.lockstep = pg.xcd_q * iris::kXcds == r.grid;
     Params pc = p;
     pc.op = d.kind;
     pc.fused = 0;

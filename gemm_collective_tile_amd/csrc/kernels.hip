@@ -51,8 +51,44 @@ __device__ __forceinline__ int xcd_id() {
   return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (15 << 11)) & (kXcds - 1);
 }
 
+// Lockstep of the GEMM rounds. An XCD's queue is dealt in blocks of Q
+// tiles, Q being the number of workgroups that work it, so round r (tiles
+// rQ .. rQ+Q-1 of the queue) is one patch of tiles whose A rows and B
+// columns meet in that XCD's L2. With the lockstep on, a workgroup starts
+// the tile of round r it took from its home queue only once every tile of
+// round r-1 of that queue has finished (whoever ran it), so the patch's
+// tiles run their K loops together. Without it the workgroups drift apart
+// over the rounds by how long each tile happens to take, and how far they
+// drift depended on the code around the tile loop: the same g2 GEMM
+// (131072 x 16384 x 16384) fetched 113 GiB from beyond L2 in one kernel
+// build and 179 GiB in another that differed only in code that never ran,
+// and at the same cycle count the chip held a 2-4 % lower clock for the
+// extra traffic. With the lockstep every build ran it in the same time. The
+// wait ends: every tile of an earlier round has been claimed, so it is held
+// by a running workgroup.
+__device__ __forceinline__ void wait_round(const Params& p, int home, int j) {
+  if (threadIdx.x == 0) {
+    const int need = (j / p.xcd_q) * p.xcd_q;
+    const int* d = p.ws + kTileDone + home * kLine;
+    uint32_t polls = 0;
+    while (ld_relaxed(d) < need) {
+      if (++polls > p.spin_limit) {
+        __hip_atomic_store(p.ws + kErr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+}
+
+// A tile taken from XCD queue q has finished (counted for the lockstep).
+__device__ __forceinline__ void tile_done(const Params& p, int q) {
+  if (p.lockstep && q >= 0 && threadIdx.x == 0) fetch_add(p.ws + kTileDone + q * kLine, 1);
+}
+
 // GEMM claim: this XCD's queue first (thread 0, one atomic), then the
-// others. `gone` (bit x: queue x seen empty) is kept in thread 0 and handed
+// others. The queue a tile came from is left in slot[3] (-1 if none). `gone` (bit x: queue x seen empty) is kept in thread 0 and handed
 // to wave 0 for the steal, so each queue's counter overshoots its share by at
 // most one per workgroup. Once the home queue is empty, lane x of wave 0
 // reads queue x's counter (one round trip for all eight) and only a queue
@@ -61,16 +97,21 @@ __device__ __forceinline__ int xcd_id() {
 // every workgroup's GEMM phase.
 __device__ __forceinline__ int claim_gemm(const Params& p, int home, uint32_t& gone, int* slot) {
   if (threadIdx.x == 0) {
-    int t = -1;
+    int t = -1, jh = -1;
     if (!(gone & (1u << home))) {
-      const int c = xcd_tile(p.xcd_q, home, fetch_add(p.ws + kCtrGemm + home * kLine, 1));
-      if (c < p.T_gemm)
+      const int j = fetch_add(p.ws + kCtrGemm + home * kLine, 1);
+      const int c = xcd_tile(p.xcd_q, home, j);
+      if (c < p.T_gemm) {
         t = c;
-      else
+        jh = j;
+      } else {
         gone |= 1u << home;
+      }
     }
     slot[0] = t;
     slot[1] = (int)gone;
+    slot[2] = jh;
+    slot[3] = t >= 0 ? home : -1;
   }
   __syncthreads();
   int v = slot[0];
@@ -92,6 +133,7 @@ __device__ __forceinline__ int claim_gemm(const Params& p, int home, uint32_t& g
       c = __shfl(c, 0);
       if (c < p.T_gemm) {
         v = c;
+        if (lane == 0) slot[3] = pick;
         break;
       }
       g |= 1u << pick;
@@ -103,7 +145,9 @@ __device__ __forceinline__ int claim_gemm(const Params& p, int home, uint32_t& g
   }
   __syncthreads();
   v = slot[0];
+  const int jh = slot[2];
   __syncthreads();
+  if (p.lockstep && jh >= p.xcd_q) wait_round(p, home, jh);
   return v;
 }
 
@@ -312,7 +356,10 @@ __device__ void wait_tiles(const Params& p, int u, int* slot, char* lds) {
           deps_open = false;
         } else {
           const int t = xcd_tile(p.xcd_q, hx, fetch_add(p.ws + kCtrGemm + hx * kLine, 1));
-          if (t < p.T_gemm) help = t;
+          if (t < p.T_gemm) {
+            help = t;
+            slot[2] = hx;
+          }
         }
       } else if (++polls > p.spin_limit) {
         __hip_atomic_store(p.ws + kErr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -326,7 +373,9 @@ __device__ void wait_tiles(const Params& p, int u, int* slot, char* lds) {
     __syncthreads();
     if (ready) return;
     if (help >= 0) {
+      const int q = slot[2];
       run_gemm_tile<OP, S>(p, help, slot, lds, rows_ready);
+      tile_done(p, q);
     } else {
       backoff(pause);
     }
@@ -355,7 +404,7 @@ template <int OP, int BM, int BN>
 __global__ __launch_bounds__(kThreads) void persistent_kernel(Params p) {
   using S = TileShape<BM, BN>;
   __shared__ __attribute__((aligned(16))) char lds[S::LDS_BYTES];
-  __shared__ int slot[2];
+  __shared__ int slot[4];
   uint64_t gs = ~0ull, ge = 0, cs = ~0ull, ce = 0;
   bool rows_ready = false;
   // shader-clock and constant-rate counters at entry (and exit, below): the
@@ -378,9 +427,11 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(Params p) {
       while (true) {
         const int t = claim_gemm(p, home, gone, slot);
         if (t < 0) break;
+        const int q = slot[3];
         const uint64_t t0 = stamp_now();
         gs = t0 < gs ? t0 : gs;
         run_gemm_tile<OP, S>(p, t, slot, lds, rows_ready);
+        tile_done(p, q);
         ge = stamp_now();
       }
     } else {

@@ -28,7 +28,8 @@ enum OpKind : int32_t {
 // fixed-size block of kStampWords words, then the int32 words
 //   GEMM queue counters (one per XCD), comm queue counter, error word (set
 //   by a wait that gave up during this launch), finished-workgroup counter,
-//   finished comm units (all_gather), status word, then from kFlagBase the
+//   finished comm units (all_gather), status word, finished tiles of each
+//   XCD queue (the lockstep of the GEMM rounds), then from kFlagBase the
 //   ready words: all_gather, one counter per GEMM row block (finished copy
 //   units of that block, kLine words apart); reduce, one flag per GEMM tile
 // Every word but the status word is zero when a persistent launch starts;
@@ -43,7 +44,8 @@ constexpr int kLine = 32;
 constexpr int kCtrGemm = 0;  // kXcds GEMM queue counters, one line each
 constexpr int kCtrComm = kXcds * kLine, kErr = kCtrComm + kLine, kDone = kErr + kLine,
               kCommDone = kDone + kLine, kStatus = kCommDone + kLine;
-constexpr int kFlagBase = kStatus + kLine;
+constexpr int kTileDone = kStatus + kLine;  // finished tiles of each XCD queue, one line each
+constexpr int kFlagBase = kTileDone + kXcds * kLine;
 // bits of the status word
 constexpr int kStatusTimeout = 1;
 constexpr int kMaxGrid = 2048;
@@ -59,6 +61,7 @@ struct Params {
   int32_t T_gemm, T_comm;
   int32_t gemm_wgs;          // pid < gemm_wgs starts on the GEMM queue
   int32_t steal;             // switch to the other queue when the first is empty
+  int32_t lockstep;          // the tiles of round r of an XCD queue start after round r-1 has finished
   int32_t fused;             // 1: flags are produced and awaited in this launch
   int32_t* ws;               // counters + flags
   uint64_t* stamps;          // [gridDim.x][4]: gemm start/end, comm start/end
