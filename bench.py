@@ -52,7 +52,7 @@ KERNEL_SOURCES = ("kernels.hip", "gemm_tile.hpp", "comm_units.hpp", "device_comm
                   "launch.hpp")
 PROFILES = os.path.join(ROOT, "profiles")
 EXTRA_WORKLOADS = ("pow2_4k", "llama7b_gate", "concurrent")
-CPU_TILES = 256             # sampled 128x128 output tiles in the CPU baseline
+CPU_TILES = 1024            # sampled 128x128 output tiles in the CPU baseline (about 10 s)
 
 
 def parse():
@@ -70,6 +70,9 @@ def parse():
     ap.add_argument("--kernel-hash", action="store_true", help="print the kernel source hash and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for HBM counter scaling)")
+    ap.add_argument("--torch-matmul", type=int, default=0, metavar="N",
+                    help="only run torch.matmul (hipBLASLt) on N x N x N fp16, --steps times, for "
+                         "comparison counters")
     return ap.parse_args()
 
 
@@ -489,6 +492,25 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "launches": 3}))
 
 
+def torch_matmul(n, steps):
+    """torch.matmul on n x n x n fp16 (the vendor library GEMM), for a counter
+    run beside the fused kernel's; prints its TFLOP/s."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(n, n, generator=g, device="cuda").to(torch.float16)
+    b = (torch.randn(n, n, generator=g, device="cuda") / n ** 0.5).to(torch.float16)
+    for _ in range(2):
+        torch.matmul(a, b)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"torch_matmul": n, "ms": round(ms, 4), "tflops": round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1)}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -500,6 +522,9 @@ def main():
         return
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.torch_matmul:
+        torch_matmul(args.torch_matmul, args.steps)
         return
     import torch
     if not torch.cuda.is_available():
