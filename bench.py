@@ -597,9 +597,10 @@ def main():
             "comm_only_gbps": w["seq_comm_only_gbps"], "comm_only_frac": w.get("seq_comm_only_hbm_frac"),
             "comm_only_cold_gbps": w["seq_comm_only_cold_gbps"],
             "copy_ceiling_gbps": ceiling,
-            "note": "gbps: fused comm window (per-workgroup stamps); comm_only: the sequential comm kernel over "
-                    "all CUs, inputs left cached by the previous step (warm) or after a 512 MiB write (cold); "
-                    "copy_ceiling: torch device-to-device copy of 1 GiB (read + write bytes)",
+            "note": "gbps: fused comm window (per-workgroup stamps); comm_only: the sequential mode's comm "
+                    "launch on all CUs (a gather beyond the 256 MiB last-level cache: the persistent kernel "
+                    "with no GEMM tiles), inputs left cached by the previous step (warm) or after a 512 MiB "
+                    "write (cold); copy_ceiling: torch device-to-device copy of 1 GiB (read + write bytes)",
         },
         "sequential_ms": w["sequential_ms"],
         "fused_vs_sequential_ms": w["fused_vs_sequential_ms"],

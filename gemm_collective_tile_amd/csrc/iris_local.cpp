@@ -659,7 +659,7 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
     comm_grid = std::min((r.grid - r.gemm_wgs) * 4, kMaxGrid);
     e = hipEventRecord(ss->fork, s);
     if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
-    if (e == hipSuccess) e = iris::launch_comm_only(pc, comm_grid, false, ss->s);
+    if (e == hipSuccess) e = iris::launch_comm_only(pc, comm_grid, ss->s);
     if (e == hipSuccess) e = iris::launch_persistent(pg, r.bm, r.bn, gemm_grid, s);
     if (e == hipSuccess) e = hipEventRecord(ss->join, ss->s);
     if (e == hipSuccess) e = hipStreamWaitEvent(s, ss->join, 0);
@@ -676,17 +676,30 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
     Params pc = p;
     pc.op = d.kind;
     pc.fused = 0;
-    // a gather larger than the 256 MiB last-level cache runs on one
-    // workgroup per CU, each with more loads in flight; a smaller one on
-    // four per CU, which start sooner
-    const bool wide = d.kind == iris::OP_AG && (double)pc.c.M * (double)pc.c.K * 2.0 > 256.0 * (1 << 20);
-    comm_grid = std::min(di.cus * (wide ? 1 : 4), kMaxGrid);
+    // A gather larger than the 256 MiB last-level cache runs as the
+    // persistent kernel with no GEMM tiles: its copy workgroups, one per CU,
+    // claim units one ahead from the shared queue (the g2 gather of 4 GiB:
+    // 6.1 TB/s warm and 5.9 cold on MI355X, against 5.5 for the comm-only
+    // kernel's fixed grid-strided units on 256 or 1024 workgroups). A smaller
+    // gather, and the reduces, start sooner on the comm-only kernel's four
+    // workgroups per CU (pow2_4k's 64 MiB: 3.6 TB/s cold against 3.4; the
+    // 8 x 64Mi all_reduce: 5.6 against 5.35).
+    const bool big_gather = d.kind == iris::OP_AG && (double)pc.c.M * (double)pc.c.K * 2.0 > 256.0 * (1 << 20);
+    comm_grid = big_gather ? r.grid : std::min(di.cus * 4, kMaxGrid);
     if (d.kind == iris::OP_AG) {
-      e = iris::launch_comm_only(pc, comm_grid, wide, s);
+      if (big_gather) {
+        Params pq = pc;
+        pq.T_gemm = 0;
+        pq.gemm_wgs = 0;
+        pq.lockstep = 0;
+        e = iris::launch_persistent(pq, r.bm, r.bn, r.grid, s);
+      } else {
+        e = iris::launch_comm_only(pc, comm_grid, s);
+      }
       if (e == hipSuccess) e = iris::launch_persistent(pg, r.bm, r.bn, r.grid, s);
     } else {
       e = iris::launch_persistent(pg, r.bm, r.bn, r.grid, s);
-      if (e == hipSuccess) e = iris::launch_comm_only(pc, comm_grid, false, s);
+      if (e == hipSuccess) e = iris::launch_comm_only(pc, comm_grid, s);
     }
     if (e != hipSuccess) return hip_fail(e, "sequential launch");
   }

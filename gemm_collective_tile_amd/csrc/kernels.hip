@@ -194,9 +194,9 @@ __device__ __forceinline__ void backoff(int& n) {
 // Unit u; with nparts > 1 only the part-th of every nparts vector groups
 // (a workgroup of the sequential comm kernel sharing the unit with others).
 // WIDE: 16 vectors per thread in flight and agent-coherent stores for the
-// all_gather copy, for one workgroup per CU (the fused kernel's copy
-// workgroups; the sequential copy kernel on a large gather); otherwise 8
-// vectors and plain stores, for four workgroups per CU.
+// all_gather copy, for one workgroup per CU (the persistent kernel's copy
+// workgroups); otherwise 8 vectors and plain stores, for the four
+// workgroups per CU of the comm-only kernel.
 template <int OP, bool WIDE = true>
 __device__ void run_comm_unit(const Params& p, int u, uint32_t part = 0, uint32_t nparts = 1) {
   const CommArgs& c = p.c;
@@ -207,10 +207,9 @@ __device__ void run_comm_unit(const Params& p, int u, uint32_t part = 0, uint32_
     const int r = u - pm * per_block;
     const int s = r / c.n_sub;
     // one workgroup per CU keeps 16 vectors per thread in flight (fused
-    // pow2_4k: copy window 14.7 -> 13.4 us on MI355X; 32 was slower; the
-    // sequential 4 GiB g2 gather: 5.25 -> 5.57 TB/s); four workgroups per CU
-    // keep 8 each (the sequential 64 MiB pow2_4k gather: 3.9 TB/s, against
-    // 3.5 on one workgroup per CU)
+    // pow2_4k: copy window 14.7 -> 13.4 us on MI355X; 32 was slower); four
+    // workgroups per CU keep 8 each (the sequential 64 MiB pow2_4k gather:
+    // 3.9 TB/s, against 3.5 on one workgroup per CU)
     ag_copy_unit<(WIDE ? 16 : 8), WIDE>(c, pm, s, r - s * c.n_sub, part, nparts);
   } else if constexpr (OP == OP_RS || OP == OP_ARMM) {
     // u = (pm * n_sub + q) * n_cc + cc
@@ -477,16 +476,23 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(Params p) {
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint64_t* st = p.stamps + (size_t)blockIdx.x * 4;
-    st[0] = gs;
-    st[1] = ge;
-    st[2] = cs;
-    st[3] = ce;
-    uint64_t* ck = p.stamps + (size_t)kMaxGrid * kClockOff + (size_t)blockIdx.x * 4;
-    ck[0] = entry[0];
-    ck[1] = entry[1];
-    ck[2] = clock64();
-    ck[3] = wall_clock64();
+    if (p.T_gemm == 0) {
+      // comm-only launch (the sequential gather): the comm kernel's stamp
+      // layout, and the GEMM launch that follows keeps its own records
+      p.comm_stamps[(size_t)blockIdx.x * 2] = cs;
+      p.comm_stamps[(size_t)blockIdx.x * 2 + 1] = ce;
+    } else {
+      uint64_t* st = p.stamps + (size_t)blockIdx.x * 4;
+      st[0] = gs;
+      st[1] = ge;
+      st[2] = cs;
+      st[3] = ce;
+      uint64_t* ck = p.stamps + (size_t)kMaxGrid * kClockOff + (size_t)blockIdx.x * 4;
+      ck[0] = entry[0];
+      ck[1] = entry[1];
+      ck[2] = clock64();
+      ck[3] = wall_clock64();
+    }
     // Every counter and flag access of this workgroup was made by this
     // thread, at agent scope; once they have completed (the drain) none can
     // follow the count below, so the last workgroup's reset cannot race
@@ -511,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(Params p) {
 }
 
 // Sequential-mode comm kernel: every unit, no flags, grid-strided.
-template <int OP, bool WIDE>
+template <int OP>
 __global__ __launch_bounds__(kThreads) void comm_only_kernel(Params p) {
   uint64_t cs = ~0ull, ce = 0;
   // fewer units than workgroups: each unit is shared by nparts workgroups
@@ -520,7 +526,7 @@ __global__ __launch_bounds__(kThreads) void comm_only_kernel(Params p) {
   for (int64_t v = blockIdx.x; v < n_virtual; v += gridDim.x) {
     if (cs == ~0ull) cs = stamp_now();
     const int u = (int)(v / nparts);
-    run_comm_unit<OP, WIDE>(p, u, (uint32_t)(v - (int64_t)u * nparts), nparts);
+    run_comm_unit<OP, false>(p, u, (uint32_t)(v - (int64_t)u * nparts), nparts);
     ce = stamp_now();
   }
   if (threadIdx.x == 0) {
@@ -562,25 +568,22 @@ hipError_t launch_persistent(const Params& p, int bm, int bn, int grid, hipStrea
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_comm_only(const Params& p, int grid, bool wide, hipStream_t s) {
+hipError_t launch_comm_only(const Params& p, int grid, hipStream_t s) {
   switch (p.op) {
     case OP_AG:
-      if (wide)
-        hipLaunchKernelGGL((comm_only_kernel<OP_AG, true>), dim3(grid), dim3(kThreads), 0, s, p);
-      else
-        hipLaunchKernelGGL((comm_only_kernel<OP_AG, false>), dim3(grid), dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL((comm_only_kernel<OP_AG>), dim3(grid), dim3(kThreads), 0, s, p);
       break;
     case OP_RS:
-      hipLaunchKernelGGL((comm_only_kernel<OP_RS, false>), dim3(grid), dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL((comm_only_kernel<OP_RS>), dim3(grid), dim3(kThreads), 0, s, p);
       break;
     case OP_ARMM:
-      hipLaunchKernelGGL((comm_only_kernel<OP_ARMM, false>), dim3(grid), dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL((comm_only_kernel<OP_ARMM>), dim3(grid), dim3(kThreads), 0, s, p);
       break;
     case OP_CONC_AR:
-      hipLaunchKernelGGL((comm_only_kernel<OP_CONC_AR, false>), dim3(grid), dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL((comm_only_kernel<OP_CONC_AR>), dim3(grid), dim3(kThreads), 0, s, p);
       break;
     case OP_CONC_COPY:
-      hipLaunchKernelGGL((comm_only_kernel<OP_CONC_COPY, false>), dim3(grid), dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL((comm_only_kernel<OP_CONC_COPY>), dim3(grid), dim3(kThreads), 0, s, p);
       break;
     default:
       return hipErrorInvalidValue;

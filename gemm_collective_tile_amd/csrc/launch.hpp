@@ -76,9 +76,7 @@ hipError_t scratch_setup(int dev, hipStream_t s, void** out);
 void* scratch_if_set_up(int dev);
 
 hipError_t launch_persistent(const Params& p, int bm, int bn, int grid, hipStream_t s);
-// wide: the all_gather copy with 16 vectors per thread in flight, for one
-// workgroup per CU (other ops ignore it)
-hipError_t launch_comm_only(const Params& p, int grid, bool wide, hipStream_t s);
+hipError_t launch_comm_only(const Params& p, int grid, hipStream_t s);
 // workgroups of the persistent kernel resident per CU, or <= 0 on error
 int persistent_blocks_per_cu(int bm, int bn, int op);
 bool tile_supported(int bm, int bn);
