@@ -70,9 +70,9 @@ def parse():
     ap.add_argument("--kernel-hash", action="store_true", help="print the kernel source hash and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for HBM counter scaling)")
-    ap.add_argument("--torch-matmul", type=int, default=0, metavar="N",
-                    help="only run torch.matmul (hipBLASLt) on N x N x N fp16, --steps times, for "
-                         "comparison counters")
+    ap.add_argument("--square-gemm", type=int, default=0, metavar="N",
+                    help="only compare the GEMM-only kernel with torch.matmul (hipBLASLt) on N x N x N "
+                         "fp16, --steps launches each")
     return ap.parse_args()
 
 
@@ -492,23 +492,57 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "launches": 3}))
 
 
-def torch_matmul(n, steps):
-    """torch.matmul on n x n x n fp16 (the vendor library GEMM), for a counter
-    run beside the fused kernel's; prints its TFLOP/s."""
+def square_gemm(n, steps):
+    """The GEMM-only kernel here against torch.matmul (the vendor library
+    GEMM) on the same n x n x n fp16 operands, in one process, each run
+    `steps` times back to back (library, ours, library again); prints both
+    rates. Ours is the sequential all_gather_matmul of 8 K-shards: its GEMM
+    launch is timed from the kernel's own stamps (the copy launch before it
+    is excluded; median of the last launch of three back-to-back runs), the
+    library's by HIP events."""
     import torch
+    import gemm_collective_tile_amd as il
     g = torch.Generator(device="cuda").manual_seed(0)
     a = torch.randn(n, n, generator=g, device="cuda").to(torch.float16)
     b = (torch.randn(n, n, generator=g, device="cuda") / n ** 0.5).to(torch.float16)
-    for _ in range(2):
-        torch.matmul(a, b)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        torch.matmul(a, b)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    print(json.dumps({"torch_matmul": n, "ms": round(ms, 4), "tflops": round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1)}))
+    shards = [t.contiguous() for t in a.split(n // 8, dim=1)]
+    bias = torch.zeros(n, dtype=torch.float16, device="cuda")
+    C = torch.empty(n, n, dtype=torch.float16, device="cuda")
+    G = torch.empty(n, n, dtype=torch.float16, device="cuda")
+    seq = il.Config(mode=il.IRIS_MODE_SEQUENTIAL)
+    flops = 2 * n ** 3
+
+    def lib():
+        for _ in range(2):
+            torch.matmul(a, b)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def ours():
+        gemm = []
+        for _ in range(3):  # steps back-to-back launch pairs, then the last GEMM launch's window
+            for _ in range(steps):
+                il.iris_ag_mm(C, G, shards, b, bias, config=seq)
+            gs, ge, _, _ = il.iris_last_windows()
+            gemm.append((ge - gs) / 1e6)
+        return statistics.median(gemm)
+
+    t_lib0 = lib()
+    t_ours = ours()
+    t_lib1 = lib()
+    il.iris_check_device_error()
+    ref = torch.matmul(a, b)
+    ok = bool(torch.equal(C, ref)) or float((C.float() - ref.float()).abs().max()) < 1e-2
+    print(json.dumps({"square_gemm": n, "torch_matmul_ms": [round(t_lib0, 4), round(t_lib1, 4)],
+                      "torch_matmul_tflops": round(flops / (min(t_lib0, t_lib1) * 1e-3) / 1e12, 1),
+                      "gemm_only_ms": round(t_ours, 4),
+                      "gemm_only_tflops": round(flops / (t_ours * 1e-3) / 1e12, 1),
+                      "clock_mhz": round(il.iris_last_clock(), 1), "agrees_with_torch": ok}))
 
 
 def main():
@@ -523,8 +557,8 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    if args.torch_matmul:
-        torch_matmul(args.torch_matmul, args.steps)
+    if args.square_gemm:
+        square_gemm(args.square_gemm, args.steps)
         return
     import torch
     if not torch.cuda.is_available():
@@ -598,8 +632,9 @@ def main():
             "comm_only_cold_gbps": w["seq_comm_only_cold_gbps"],
             "copy_ceiling_gbps": ceiling,
             "note": "gbps: fused comm window (per-workgroup stamps); comm_only: the sequential mode's comm "
-                    "launch on all CUs (a gather beyond the 256 MiB last-level cache: the persistent kernel "
-                    "with no GEMM tiles), inputs left cached by the previous step (warm) or after a 512 MiB "
+                    "launch on all CUs (a gather beyond the 256 MiB last-level cache: gather_only_kernel, the "
+                    "persistent kernel's copy workgroups alone), inputs left cached by the previous step (warm) "
+                    "or after a 512 MiB "
                     "write (cold); copy_ceiling: torch device-to-device copy of 1 GiB (read + write bytes)",
         },
         "sequential_ms": w["sequential_ms"],
