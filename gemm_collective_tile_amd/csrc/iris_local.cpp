@@ -676,8 +676,8 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
     Params pc = p;
     pc.op = d.kind;
     pc.fused = 0;
-    // A gather larger than the 256 MiB last-level cache runs as the
-    // persistent kernel with no GEMM tiles: its copy workgroups, one per CU,
+    // A gather larger than the 256 MiB last-level cache runs on the
+    // persistent kernel's body with no GEMM tiles: its copy workgroups, one per CU,
     // claim units one ahead from the shared queue (the g2 gather of 4 GiB:
     // 6.1 TB/s warm and 5.9 cold on MI355X, against 5.5 for the comm-only
     // kernel's fixed grid-strided units on 256 or 1024 workgroups). A smaller
@@ -692,7 +692,7 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
         pq.T_gemm = 0;
         pq.gemm_wgs = 0;
         pq.lockstep = 0;
-        e = iris::launch_persistent(pq, r.bm, r.bn, r.grid, s);
+        e = iris::launch_gather_only(pq, r.bm, r.bn, r.grid, s);
       } else {
         e = iris::launch_comm_only(pc, comm_grid, s);
       }

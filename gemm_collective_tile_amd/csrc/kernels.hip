@@ -405,8 +405,11 @@ __device__ void run_gemm_tile(const Params& p, int t, int* slot, char* lds, bool
 }
 
 // ----------------------------------------------------------------- kernels
+// The persistent kernel's body. Two kernels run it: persistent_kernel for
+// every op, and gather_only_kernel for the sequential all_gather's copy
+// (T_gemm = 0), whose launches then show apart from the GEMM's in traces.
 template <int OP, int BM, int BN>
-__global__ __launch_bounds__(kThreads) void persistent_kernel(Params p) {
+__device__ __forceinline__ void persistent_body(const Params& p) {
   using S = TileShape<BM, BN>;
   __shared__ __attribute__((aligned(16))) char lds[S::LDS_BYTES];
   __shared__ int slot[4];
@@ -516,6 +519,16 @@ __global__ __launch_bounds__(kThreads) void persistent_kernel(Params p) {
   }
 }
 
+template <int OP, int BM, int BN>
+__global__ __launch_bounds__(kThreads) void persistent_kernel(Params p) {
+  persistent_body<OP, BM, BN>(p);
+}
+
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads) void gather_only_kernel(Params p) {
+  persistent_body<OP_AG, BM, BN>(p);
+}
+
 // Sequential-mode comm kernel: every unit, no flags, grid-strided.
 template <int OP>
 __global__ __launch_bounds__(kThreads) void comm_only_kernel(Params p) {
@@ -565,6 +578,21 @@ hipError_t launch_persistent(const Params& p, int bm, int bn, int grid, hipStrea
   if (bm == 256 && bn == 128) return launch_op<256, 128>(p, grid, s);
   if (bm == 128 && bn == 128) return launch_op<128, 128>(p, grid, s);
   if (bm == 64 && bn == 64) return launch_op<64, 64>(p, grid, s);
+  return hipErrorInvalidValue;
+}
+
+template <int BM, int BN>
+static hipError_t launch_gather_tile(const Params& p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((gather_only_kernel<BM, BN>), dim3(grid), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_only(const Params& p, int bm, int bn, int grid, hipStream_t s) {
+  if (p.op != OP_AG || p.T_gemm != 0) return hipErrorInvalidValue;
+  if (bm == 256 && bn == 256) return launch_gather_tile<256, 256>(p, grid, s);
+  if (bm == 256 && bn == 128) return launch_gather_tile<256, 128>(p, grid, s);
+  if (bm == 128 && bn == 128) return launch_gather_tile<128, 128>(p, grid, s);
+  if (bm == 64 && bn == 64) return launch_gather_tile<64, 64>(p, grid, s);
   return hipErrorInvalidValue;
 }
 

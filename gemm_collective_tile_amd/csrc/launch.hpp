@@ -77,6 +77,9 @@ void* scratch_if_set_up(int dev);
 
 hipError_t launch_persistent(const Params& p, int bm, int bn, int grid, hipStream_t s);
 hipError_t launch_comm_only(const Params& p, int grid, hipStream_t s);
+// the persistent kernel's copy workgroups alone (op OP_AG, T_gemm = 0), under
+// its own kernel name
+hipError_t launch_gather_only(const Params& p, int bm, int bn, int grid, hipStream_t s);
 // workgroups of the persistent kernel resident per CU, or <= 0 on error
 int persistent_blocks_per_cu(int bm, int bn, int op);
 bool tile_supported(int bm, int bn);
