@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--gemm-wgs", type=int, default=0,
                     help="fixed gemm_wgs for the headline workload (no sweep)")
+    ap.add_argument("--no-lockstep", action="store_true",
+                    help="headline without the GEMM rounds' lockstep (IRIS_FLAG_NO_LOCKSTEP; with "
+                         "--gemm-wgs, for comparison runs)")
     ap.add_argument("--kernel-hash", action="store_true", help="print the kernel source hash and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for HBM counter scaling)")
@@ -170,7 +173,7 @@ def windows(case):
     return g, c
 
 
-def measure(name, steps, warmup, sweep, fixed_wgs=0):
+def measure(name, steps, warmup, sweep, fixed_wgs=0, flags=0):
     il = __import__("gemm_collective_tile_amd")
     case = Case(name)
     w = case.w
@@ -183,14 +186,14 @@ def measure(name, steps, warmup, sweep, fixed_wgs=0):
         best, sweep_ms = il.iris_tune_gemm_wgs(case.op, cands, reps=5, **case.tune_kw)
         shape = {k: v for k, v in case.tune_kw.items() if k in ("W", "rank", "M", "N", "K", "comm_elems")}
         pred_best, pred_ms = il.iris_predict_gemm_wgs(case.op, cands, case.G_wgs, **shape)
-    cfg = Config(gemm_wgs=best or 0)
+    cfg = Config(gemm_wgs=best or 0, flags=flags)
     log(f"[{name}] timing fused mode, gemm_wgs={best}")
     wall_ms, mean_ms = time_steps(case, cfg, steps, warmup)
     case.step(cfg)
     gwin, cwin = windows(case)
     clock_mhz = il.iris_last_clock()
     log(f"[{name}] timing sequential mode")
-    seq_cfg = Config(mode=il.IRIS_MODE_SEQUENTIAL)
+    seq_cfg = Config(mode=il.IRIS_MODE_SEQUENTIAL, flags=flags)
     case.step(seq_cfg)
     case.step(seq_cfg)
     sgwin, scwin = windows(case)
@@ -565,7 +568,14 @@ def main():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(1)
     failures = []
-    head, case = measure(args.workload, args.steps, args.warmup, not args.no_sweep, args.gemm_wgs)
+    import gemm_collective_tile_amd as il
+    il_flags = il.IRIS_FLAG_NO_LOCKSTEP if args.no_lockstep else 0
+    if args.no_lockstep and not args.gemm_wgs:
+        print("--no-lockstep needs --gemm-wgs (the sweep runs with the lockstep)", file=sys.stderr)
+        sys.exit(2)
+    head, case = measure(args.workload, args.steps, args.warmup, not args.no_sweep, args.gemm_wgs, il_flags)
+    if args.no_lockstep:
+        head["flags"] = "IRIS_FLAG_NO_LOCKSTEP"
     cpu = None
     if not args.no_check:
         log(f"[{args.workload}] oracle check")

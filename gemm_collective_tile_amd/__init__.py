@@ -33,6 +33,7 @@ IRIS_MODE_SEQUENTIAL = 1
 IRIS_MODE_TWO_STREAM = 2
 IRIS_FLAG_NO_STEAL = 1
 IRIS_FLAG_BIAS_ALONG_M = 2
+IRIS_FLAG_NO_LOCKSTEP = 4
 IRIS_OP_AG_MM = 1
 IRIS_OP_MM_RS = 2
 IRIS_OP_MM_AR = 3

@@ -294,7 +294,7 @@ int resolve_static(const iris_config_t* cfg, Resolved* r) {
   if (r->comm_chunk % 2048 != 0) return fail(IRIS_ERR_CONFIG, "comm_chunk must be a multiple of 2048 (got %d)", r->comm_chunk);
   if (r->mode != IRIS_MODE_FUSED && r->mode != IRIS_MODE_SEQUENTIAL && r->mode != IRIS_MODE_TWO_STREAM)
     return fail(IRIS_ERR_CONFIG, "unknown mode %d", r->mode);
-  if (r->flags & ~(IRIS_FLAG_NO_STEAL | IRIS_FLAG_BIAS_ALONG_M))
+  if (r->flags & ~(IRIS_FLAG_NO_STEAL | IRIS_FLAG_BIAS_ALONG_M | IRIS_FLAG_NO_LOCKSTEP))
     return fail(IRIS_ERR_CONFIG, "unknown flag bits 0x%x", r->flags);
   return IRIS_OK;
 }
@@ -634,7 +634,7 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
     // lockstep rounds only where an XCD queue is dealt in blocks of the
     // workgroups that work it: beside an independent collective more
     // workgroups join the GEMM than the blocks were sized for
-    p.lockstep = p.xcd_q * iris::kXcds == r.grid;
+    p.lockstep = p.xcd_q * iris::kXcds == r.grid && !(r.flags & IRIS_FLAG_NO_LOCKSTEP);
     e = iris::launch_persistent(p, r.bm, r.bn, r.grid, s);
     if (e != hipSuccess) return hip_fail(e, "fused launch");
   } else if (r.mode == IRIS_MODE_TWO_STREAM) {
@@ -651,7 +651,7 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
     pg.T_comm = 0;
     pg.gemm_wgs = r.gemm_wgs;
     pg.xcd_q = std::max(1, r.gemm_wgs / iris::kXcds);
-    pg.lockstep = pg.xcd_q * iris::kXcds == r.gemm_wgs;
+    pg.lockstep = pg.xcd_q * iris::kXcds == r.gemm_wgs && !(r.flags & IRIS_FLAG_NO_LOCKSTEP);
     Params pc = p;
     pc.op = d.kind;
     pc.fused = 0;
@@ -672,7 +672,7 @@ int run(const OpDesc& d, const iris_config_t* cfg, void* workspace, size_t ws_by
     pg.fused = 0;
     pg.T_comm = 0;
     pg.gemm_wgs = r.grid;
-    pg.lockstep = pg.xcd_q * iris::kXcds == r.grid;
+    pg.lockstep = pg.xcd_q * iris::kXcds == r.grid && !(r.flags & IRIS_FLAG_NO_LOCKSTEP);
     Params pc = p;
     pc.op = d.kind;
     pc.fused = 0;

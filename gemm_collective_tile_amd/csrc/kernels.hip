@@ -59,13 +59,12 @@ __device__ __forceinline__ int xcd_id() {
 // round r-1 of that queue has finished (whoever ran it), so the patch's
 // tiles run their K loops together. Without it the workgroups drift apart
 // over the rounds by how long each tile happens to take, and how far they
-// drift depended on the code around the tile loop: the same g2 GEMM
-// (131072 x 16384 x 16384) fetched 113 GiB from beyond L2 in one kernel
-// build and 179 GiB in another that differed only in code that never ran,
-// and at the same cycle count the chip held a 2-4 % lower clock for the
-// extra traffic. With the lockstep every build ran it in the same time. The
-// wait ends: every tile of an earlier round has been claimed, so it is held
-// by a running workgroup.
+// drift depended on the code around the tile loop. On MI355X, the fused g2
+// op (131072 x 16384 x 16384, gemm_wgs 128) without the lockstep
+// (IRIS_FLAG_NO_LOCKSTEP) read 293 GiB from beyond L2 against 118 GiB with
+// it, and at about the same cycle count the chip held an 8 % lower clock for
+// the extra traffic: 62.1 against 57.5 ms. The wait ends: every tile of an
+// earlier round has been claimed, so it is held by a running workgroup.
 __device__ __forceinline__ void wait_round(const Params& p, int home, int j) {
   if (threadIdx.x == 0) {
     const int need = (j / p.xcd_q) * p.xcd_q;

@@ -105,6 +105,10 @@ typedef enum iris_status {
 /* config flags */
 #define IRIS_FLAG_NO_STEAL 1     /* workgroups stay on their first queue */
 #define IRIS_FLAG_BIAS_ALONG_M 2 /* bias has M entries instead of N */
+#define IRIS_FLAG_NO_LOCKSTEP 4  /* GEMM rounds of an XCD queue may overlap (no
+                                    wait for the previous round's tiles);
+                                    same results, for measuring what the
+                                    lockstep saves */
 
 /* op ids (workspace sizing, tuning) */
 #define IRIS_OP_AG_MM 1

@@ -89,7 +89,8 @@ def test_ag_mm_several_waves_any_split():
     join the GEMM only once every copy unit has finished. The gathered matrix
     is bit-exact, C matches the oracle, and C is bit-identical across splits
     that start one, some or all but one workgroup on the GEMM, and against
-    sequential mode, with copy units of the default size and of one row."""
+    sequential mode, with copy units of the default size and of one row, and
+    with the GEMM rounds' lockstep switched off."""
     inp = ag_inputs(4196, 4160, 256, 4, seed=21)
     g_ref, c_ref = oracle_ag(inp)
     for tile in [(256, 256), (128, 128)]:
@@ -99,14 +100,16 @@ def test_ag_mm_several_waves_any_split():
         first = None
         # comm_block_m = 1: 4196 * 4 one-row copy units, dozens per workgroup,
         # so the comm loop claims units ahead
-        for gw, mode, rows in [(1, il.IRIS_MODE_FUSED, 0), (G // 8, il.IRIS_MODE_FUSED, 0),
-                               (G // 2, il.IRIS_MODE_FUSED, 0), (G - 1, il.IRIS_MODE_FUSED, 0),
-                               (1, il.IRIS_MODE_FUSED, 1), (G // 2, il.IRIS_MODE_FUSED, 1),
-                               (0, il.IRIS_MODE_SEQUENTIAL, 0)]:
+        free = il.IRIS_FLAG_NO_LOCKSTEP
+        for gw, mode, rows, fl in [(1, il.IRIS_MODE_FUSED, 0, 0), (G // 8, il.IRIS_MODE_FUSED, 0, 0),
+                                   (G // 2, il.IRIS_MODE_FUSED, 0, 0), (G - 1, il.IRIS_MODE_FUSED, 0, 0),
+                                   (1, il.IRIS_MODE_FUSED, 1, 0), (G // 2, il.IRIS_MODE_FUSED, 1, 0),
+                                   (0, il.IRIS_MODE_SEQUENTIAL, 0, 0), (G // 2, il.IRIS_MODE_FUSED, 0, free),
+                                   (0, il.IRIS_MODE_SEQUENTIAL, 0, free)]:
             note(f"ag_mm several waves tile={tile} grid={G} tiles={n_tiles} gemm_wgs={gw} mode={mode} "
-                 f"comm_block_m={rows}")
+                 f"comm_block_m={rows} flags={fl}")
             C, Gb = run_ag(inp, Config(block_m=tile[0], block_n=tile[1], gemm_wgs=gw, mode=mode,
-                                       comm_block_m=rows))
+                                       comm_block_m=rows, flags=fl))
             assert_bits_equal(Gb, g_ref, f"gathered tile={tile} gemm_wgs={gw}")
             if first is None:
                 assert_close(C, c_ref, f"C tile={tile}")
