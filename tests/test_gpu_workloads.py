@@ -164,6 +164,16 @@ def test_g2_all_gather_matmul():
     torch.cuda.synchronize()
     assert_same_bits(C2, C, "g2 C, gemm_wgs=1 against the default split")
     assert_same_bits(G2, G, "g2 gathered, gemm_wgs=1 against the default split")
+    # sequential mode: the 4 GiB gather runs alone (gather_only_kernel), then
+    # the GEMM-only kernel; bit-identical to the fused op
+    note("g2 sequential all_gather_matmul")
+    C2.fill_(float("nan"))
+    G2.fill_(float("nan"))
+    il.iris_ag_mm(C2, G2, inp["shards"], inp["B"], inp["bias"], config=Config(mode=il.IRIS_MODE_SEQUENTIAL))
+    torch.cuda.synchronize()
+    il.iris_check_device_error()
+    assert_same_bits(C2, C, "g2 C, sequential against fused")
+    assert_same_bits(G2, G, "g2 gathered, sequential against fused")
     del C2, G2
     note("g2: full gathered buffer")
     check_gathered(G, inp["shards"])
