@@ -92,7 +92,9 @@ typedef enum iris_status {
 #define IRIS_MODE_FUSED 0      /* one persistent kernel, two work queues */
 #define IRIS_MODE_SEQUENTIAL 1 /* comm kernel and GEMM kernel, one after the
                                   other on the same stream, each on the whole
-                                  GPU (the unfused baseline) */
+                                  GPU (the unfused baseline); an all_gather
+                                  larger than 256 MiB runs its copy on the
+                                  persistent kernel's copy workgroups alone */
 #define IRIS_MODE_TWO_STREAM 2 /* GEMM kernel on gemm_wgs workgroups on the
                                   caller's stream, comm kernel beside it on a
                                   second stream of the library's; only for ops
