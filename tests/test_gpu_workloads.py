@@ -147,6 +147,38 @@ def test_concurrent_gemm_and_all_reduce():
                                                                    cols=(c0, c1)), "concurrent C")
 
 
+def test_sequential_large_gather_ragged():
+    """A gathered buffer beyond the 256 MiB last-level cache takes the
+    sequential mode's large-gather path (the persistent kernel's copy
+    workgroups alone, then the GEMM-only kernel). Here with W = 3 and ragged
+    M, N and K (a 77-row last row block, a 40-column last column block, K not
+    a multiple of the 64-deep K step): sequential and fused bit-identical, the
+    whole gathered buffer bit-exact, sampled tiles (the ragged corner among
+    them) within tolerance of the oracle."""
+    K_local = 2824
+    w = wl.Workload("ragged_large_gather", "ag_mm", M=16461, N=296, K=3 * K_local, W=3, a_std=1.0,
+                    b_std=(3 * K_local) ** -0.5)
+    assert w.M * w.K * 2 > 256 << 20
+    inp = wl.make_inputs(w, seed=5, device="cuda")
+    note("ragged large gather: sequential all_gather_matmul 16461x296x8472, W=3")
+    C = torch.full((w.M, w.N), float("nan"), dtype=torch.float16, device="cuda")
+    G = torch.full((w.M, w.K), float("nan"), dtype=torch.float16, device="cuda")
+    il.iris_ag_mm(C, G, inp["shards"], inp["B"], inp["bias"], config=Config(mode=il.IRIS_MODE_SEQUENTIAL))
+    torch.cuda.synchronize()
+    il.iris_check_device_error()
+    note("ragged large gather: fused")
+    C2, G2 = torch.full_like(C, float("nan")), torch.full_like(G, float("nan"))
+    il.iris_ag_mm(C2, G2, inp["shards"], inp["B"], inp["bias"])
+    torch.cuda.synchronize()
+    il.iris_check_device_error()
+    assert_same_bits(C2, C, "ragged large gather C, fused against sequential")
+    assert_same_bits(G2, G, "ragged large gather gathered, fused against sequential")
+    del C2, G2
+    note("ragged large gather: full gathered buffer, sampled tiles of C")
+    check_gathered(G, inp["shards"])
+    check_sampled_tiles(C, ag_tile_ref(inp), "ragged large gather C")
+
+
 def test_g2_all_gather_matmul():
     w = wl.WORKLOADS["g2"]
     inp = wl.make_inputs(w, seed=0, device="cuda")
