@@ -431,6 +431,17 @@ def copy_ceiling():
     return round(2 * 2 * n / (ms * 1e-3) / 1e9, 1)
 
 
+def mfma_ceiling():
+    """The dense fp16 MFMA rate of this GPU with no memory traffic
+    (iris_mfma_ceiling): random operands switching every instruction, as on
+    GEMM data, and constant ones; TFLOP/s and the clock each held."""
+    import gemm_collective_tile_amd as il
+    rt, rm = il.iris_mfma_ceiling(random_operands=True, iters=400000)
+    ct, cm = il.iris_mfma_ceiling(random_operands=False, iters=400000)
+    return {"random_operands_tflops": round(rt, 1), "random_operands_clock_mhz": round(rm, 1),
+            "constant_operands_tflops": round(ct, 1), "constant_operands_clock_mhz": round(cm, 1)}
+
+
 def strip_comments(src):
     """C++ source without // and /* */ comments and with runs of blank space
     collapsed, so that a comment edit leaves the hash of the code alone."""
@@ -590,6 +601,8 @@ def main():
     del case
     torch.cuda.empty_cache()
     ceiling = copy_ceiling()
+    log("MFMA ceiling (register operands, no memory traffic)")
+    mfma_ceil = mfma_ceiling()
     extra = []
     if not args.headline_only:
         for name in EXTRA_WORKLOADS + ("g2",):
@@ -634,6 +647,11 @@ def main():
             "kernel": f"persistent_kernel<1,256,256> (fused {w['op']}), HIP-event mean over {args.steps} "
                       f"back-to-back launches: {w['kernel_ms']} ms",
             "clock_mhz": w["clock_mhz"], "frac_at_clock": w.get("mfma_frac_at_clock"),
+            "mfma_ceiling": mfma_ceil,
+            "frac_of_ceiling": round(w["kernel_tflops"] / mfma_ceil["random_operands_tflops"], 4),
+            "ceiling_note": "mfma_ceiling: iris_mfma_ceiling, MFMAs on register operands with no memory "
+                            "traffic; random fp16 operands switching every instruction (as on GEMM data) hold "
+                            "the chip at its package power limit, constant ones do not",
         },
         "comm": {
             "gbps": w["comm_gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": w.get("comm_hbm_frac"),

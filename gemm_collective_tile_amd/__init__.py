@@ -130,6 +130,7 @@ def _load() -> ctypes.CDLL:
         "iris_last_windows": [vp, vp] + [ctypes.POINTER(ctypes.c_double)] * 4,
         "iris_check_device_error": [vp, vp],
         "iris_last_clock": [vp, vp, ctypes.POINTER(ctypes.c_double)],
+        "iris_mfma_ceiling": [i32, i32, vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)],
         "iris_device_info": [i32, ctypes.POINTER(_DeviceInfo)],
         "iris_status_str": [i32],
         "iris_last_error_message": [],
@@ -471,6 +472,16 @@ def iris_last_clock(workspace=None, stream=None) -> float:
     ws, _ = _ws(workspace)
     _check(_lib.iris_last_clock(ws, _stream(stream), ctypes.byref(v)))
     return v.value
+
+
+def iris_mfma_ceiling(random_operands: bool = True, iters: int = 400000, stream=None):
+    """(TFLOP/s, MHz): the dense fp16 MFMA rate of the current GPU with no
+    memory traffic, operands random (switching as on GEMM data) or constant,
+    and the shader clock it held. Waits for the run."""
+    t, m = ctypes.c_double(), ctypes.c_double()
+    _check(_lib.iris_mfma_ceiling(1 if random_operands else 0, int(iters), _stream(stream), ctypes.byref(t),
+                                  ctypes.byref(m)))
+    return t.value, m.value
 
 
 def iris_check_device_error(workspace=None, stream=None) -> None:

@@ -23,7 +23,7 @@ COMMON = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wall", "-Wno-unused-command-line-argument",
 ]
-SOURCES = ["kernels.hip", "iris_local.cpp", "predict.cpp"]
+SOURCES = ["kernels.hip", "iris_local.cpp", "predict.cpp", "mfma_ceiling.hip"]
 
 
 def _compile(src: str, verbose: bool) -> str:

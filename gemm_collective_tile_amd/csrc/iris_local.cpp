@@ -29,6 +29,7 @@
 #include <vector>
 
 #include "launch.hpp"
+#include "mfma_ceiling.hpp"
 
 namespace {
 
@@ -1182,6 +1183,27 @@ int iris_last_clock(void* workspace, void* stream, double* mhz) {
     }
   }
   if (ticks > 0) *mhz = cycles / ticks * (double)di.wall_khz / 1e3;
+  return IRIS_OK;
+}
+
+int iris_mfma_ceiling(int32_t random_operands, int32_t iters, void* stream, double* tflops, double* clock_mhz) {
+  g_msg.clear();
+  if (!tflops || !clock_mhz) return fail(IRIS_ERR_INVALID_ARG, "tflops and clock_mhz must not be NULL");
+  *tflops = -1.0;
+  *clock_mhz = -1.0;
+  if (iters < 1 || iters > (1 << 24)) return fail(IRIS_ERR_INVALID_ARG, "iters must be in [1, 2^24] (got %d)", iters);
+  int dev = 0;
+  DevInfo di;
+  int st = current_device(&dev, &di);
+  if (st) return st;
+  const int grid = di.cus * 4;
+  float ms = 0.0f;
+  double cycles = 0.0, ticks = 0.0;
+  const hipError_t e =
+      iris::mfma_ceiling_run(random_operands != 0, iters, grid, (hipStream_t)stream, &ms, &cycles, &ticks);
+  if (e != hipSuccess) return hip_fail(e, "MFMA ceiling launch");
+  if (ms > 0.0f) *tflops = iris::kCeilingFlopPerTrip * (double)iters * (double)grid / ((double)ms * 1e-3) / 1e12;
+  if (ticks > 0.0) *clock_mhz = cycles / ticks * (double)di.wall_khz / 1e3;
   return IRIS_OK;
 }
 

@@ -397,6 +397,24 @@ int iris_last_windows(void* workspace, void* stream, double* gemm_start_ns,
 int iris_last_clock(void* workspace, void* stream, double* mhz);
 
 /*
+ * Measurement helper (no counterpart on the pages): the dense fp16 MFMA rate
+ * of the current device with no memory traffic, the achievable ceiling that
+ * the GEMM's rate is compared with beside the published peak.
+ * CUs x 4 workgroups of 4 waves each run `iters` trips of eight
+ * v_mfma_f32_32x32x16_f16 on eight independent accumulators, operands in
+ * registers: random fp16 values that change from one instruction to the
+ * next if `random_operands` is non-zero (the multipliers then switch as on
+ * GEMM data), else constants. One short warm-up launch, then one timed
+ * launch on `stream`; waits for it. Allocates and frees two small device
+ * buffers.
+ *   *tflops     FLOP of the timed launch / its duration (HIP events)
+ *   *clock_mhz  shader clock held, from the kernel's own counters
+ * Errors: IRIS_ERR_INVALID_ARG (NULL outputs; iters outside [1, 2^24], checked
+ * before any HIP call), IRIS_ERR_HIP. Outputs are -1 on error.
+ */
+int iris_mfma_ceiling(int32_t random_operands, int32_t iters, void* stream, double* tflops, double* clock_mhz);
+
+/*
  * Device-side errors since the last check on `workspace` (NULL: the
  * library's own workspace for `stream` and the device's static scratch of
  * iris_ag_mm_noalloc). Waits for `stream`, then returns

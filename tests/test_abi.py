@@ -165,3 +165,12 @@ def test_grid_size_rejects_unknown_op(lib):
     # the op is checked before the device is queried
     assert lib.iris_grid_size(99, None) == -1
     assert "unknown op" in lib.iris_last_error_message().decode()
+
+
+def test_mfma_ceiling_checks_arguments_before_any_device_call(lib):
+    t, m = ctypes.c_double(7.0), ctypes.c_double(7.0)
+    for iters in (0, -1, (1 << 24) + 1):
+        assert lib.iris_mfma_ceiling(1, iters, None, ctypes.byref(t), ctypes.byref(m)) == 1
+        assert t.value == -1.0 and m.value == -1.0
+    assert lib.iris_mfma_ceiling(1, 10, None, None, ctypes.byref(m)) == 1
+    assert "NULL" in lib.iris_last_error_message().decode()
