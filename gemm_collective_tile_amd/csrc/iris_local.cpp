@@ -1191,7 +1191,7 @@ int iris_mfma_ceiling(int32_t random_operands, int32_t iters, void* stream, doub
   if (!tflops || !clock_mhz) return fail(IRIS_ERR_INVALID_ARG, "tflops and clock_mhz must not be NULL");
   *tflops = -1.0;
   *clock_mhz = -1.0;
-  if (iters < 1 || iters > (1 << 24)) return fail(IRIS_ERR_INVALID_ARG, "iters must be in [1, 2^24] (got %d)", iters);
+  if (iters < 1 || iters > (1 << 22)) return fail(IRIS_ERR_INVALID_ARG, "iters must be in [1, 2^22] (got %d)", iters);
   int dev = 0;
   DevInfo di;
   int st = current_device(&dev, &di);

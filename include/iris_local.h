@@ -409,7 +409,7 @@ int iris_last_clock(void* workspace, void* stream, double* mhz);
  * buffers.
  *   *tflops     FLOP of the timed launch / its duration (HIP events)
  *   *clock_mhz  shader clock held, from the kernel's own counters
- * Errors: IRIS_ERR_INVALID_ARG (NULL outputs; iters outside [1, 2^24], checked
+ * Errors: IRIS_ERR_INVALID_ARG (NULL outputs; iters outside [1, 2^22], checked
  * before any HIP call), IRIS_ERR_HIP. Outputs are -1 on error.
  */
 int iris_mfma_ceiling(int32_t random_operands, int32_t iters, void* stream, double* tflops, double* clock_mhz);
