@@ -474,8 +474,15 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+# template argument of persistent_kernel<OP, BM, BN> for each op, and the
+# prefix of its profile files
+KERNEL_OP = {"ag_mm": (1, "ag"), "mm_rs": (2, "rs"), "mm_ar": (3, "ar"), "concurrent": (4, "ar")}
+
+
 def traffic_file(workload):
-    return os.path.join(PROFILES, f"persistent_kernel_ag_{workload}_traffic.txt")
+    import workloads as wl
+    op = wl.WORKLOADS[workload].op if workload in wl.WORKLOADS else "ag_mm"
+    return os.path.join(PROFILES, f"persistent_kernel_{KERNEL_OP[op][1]}_{workload}_traffic.txt")
 
 
 def recorded_traffic(workload):
@@ -643,9 +650,11 @@ def main():
             "frac": w["mfma_frac"], "traffic": recorded_traffic(w["workload"]),
             "traffic_note": "bytes fetched from beyond L2 (HBM and last-level cache hits) plus bytes written, "
                             "per launch, rocprofv3 FETCH_SIZE/WRITE_SIZE scaled by a plain copy; "
-                            f"profiles/{os.path.basename(traffic_file(w['workload']))}",
-            "kernel": f"persistent_kernel<1,256,256> (fused {w['op']}), HIP-event mean over {args.steps} "
-                      f"back-to-back launches: {w['kernel_ms']} ms",
+                            + (f"profiles/{os.path.basename(traffic_file(w['workload']))}"
+                               if os.path.exists(traffic_file(w["workload"])) else
+                               "not recorded in this form for this workload"),
+            "kernel": f"persistent_kernel<{KERNEL_OP[w['op']][0]},256,256> (fused {w['op']}), HIP-event mean over "
+                      f"{args.steps} back-to-back launches: {w['kernel_ms']} ms",
             "clock_mhz": w["clock_mhz"], "frac_at_clock": w.get("mfma_frac_at_clock"),
             "mfma_ceiling": mfma_ceil,
             "frac_of_ceiling": round(w["kernel_tflops"] / mfma_ceil["random_operands_tflops"], 4),
