@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--square-gemm", type=int, default=0, metavar="N",
                     help="only compare the GEMM-only kernel with torch.matmul (hipBLASLt) on N x N x N "
                          "fp16, --steps launches each")
+    ap.add_argument("--gemm-shape", default="", metavar="M,N,K",
+                    help="the same comparison on M x N x K (K a multiple of 64), e.g. the g2 shape "
+                         "131072,16384,16384")
     return ap.parse_args()
 
 
@@ -513,9 +516,9 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "launches": 3}))
 
 
-def square_gemm(n, steps):
+def square_gemm(m, n, k, steps):
     """The GEMM-only kernel here against torch.matmul (the vendor library
-    GEMM) on the same n x n x n fp16 operands, in one process, each run
+    GEMM) on the same m x n x k fp16 operands, in one process, each run
     `steps` times back to back (library, ours, library again); prints both
     rates. Ours is the sequential all_gather_matmul of 8 K-shards: its GEMM
     launch is timed from the kernel's own stamps (the copy launch before it
@@ -524,14 +527,14 @@ def square_gemm(n, steps):
     import torch
     import gemm_collective_tile_amd as il
     g = torch.Generator(device="cuda").manual_seed(0)
-    a = torch.randn(n, n, generator=g, device="cuda").to(torch.float16)
-    b = (torch.randn(n, n, generator=g, device="cuda") / n ** 0.5).to(torch.float16)
-    shards = [t.contiguous() for t in a.split(n // 8, dim=1)]
+    a = torch.randn(m, k, generator=g, device="cuda").to(torch.float16)
+    b = (torch.randn(k, n, generator=g, device="cuda") / k ** 0.5).to(torch.float16)
+    shards = [t.contiguous() for t in a.split(k // 8, dim=1)]
     bias = torch.zeros(n, dtype=torch.float16, device="cuda")
-    C = torch.empty(n, n, dtype=torch.float16, device="cuda")
-    G = torch.empty(n, n, dtype=torch.float16, device="cuda")
+    C = torch.empty(m, n, dtype=torch.float16, device="cuda")
+    G = torch.empty(m, k, dtype=torch.float16, device="cuda")
     seq = il.Config(mode=il.IRIS_MODE_SEQUENTIAL)
-    flops = 2 * n ** 3
+    flops = 2 * m * n * k
 
     def lib():
         for _ in range(2):
@@ -559,7 +562,7 @@ def square_gemm(n, steps):
     il.iris_check_device_error()
     ref = torch.matmul(a, b)
     ok = bool(torch.equal(C, ref)) or float((C.float() - ref.float()).abs().max()) < 1e-2
-    print(json.dumps({"square_gemm": n, "torch_matmul_ms": [round(t_lib0, 4), round(t_lib1, 4)],
+    print(json.dumps({"gemm_shape": [m, n, k], "torch_matmul_ms": [round(t_lib0, 4), round(t_lib1, 4)],
                       "torch_matmul_tflops": round(flops / (min(t_lib0, t_lib1) * 1e-3) / 1e12, 1),
                       "gemm_only_ms": round(t_ours, 4),
                       "gemm_only_tflops": round(flops / (t_ours * 1e-3) / 1e12, 1),
@@ -579,7 +582,11 @@ def main():
         copy_calibration()
         return
     if args.square_gemm:
-        square_gemm(args.square_gemm, args.steps)
+        square_gemm(args.square_gemm, args.square_gemm, args.square_gemm, args.steps)
+        return
+    if args.gemm_shape:
+        m, n, k = (int(x) for x in args.gemm_shape.split(","))
+        square_gemm(m, n, k, args.steps)
         return
     import torch
     if not torch.cuda.is_available():
